@@ -1,0 +1,9 @@
+"""CPU oracle for MX block quantization (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package. The library in
+``microscaling_block_quantized_amd`` never imports it, and it imports nothing
+from the library.
+"""
+from .mx_oracle import *  # noqa: F401,F403
+from .mx_oracle import __all__  # noqa: F401
