@@ -1,0 +1,180 @@
+"""Throughput of the fused row+column MXFP8 cast on one MI355X.
+
+Workload: a 16384x4096 BF16 activation tensor (N(0,1) with 4 outlier columns
+x100, seeded, synthetic), quantized to MXFP8 E4M3 with the OCP floor scale
+rule, row-wise and column-wise (transposed) copies emitted by one kernel. One
+step = one such cast over one tensor, inputs already resident in HBM. Three
+input/output buffer sets rotate so the 816 MB working set exceeds the 256 MB
+last-level cache.
+
+Prints one JSON line. `value` is GB/s of algorithmic traffic (each input byte
+read once, each code and scale byte written once: 272,629,760 B per step).
+`roofline` compares that rate with MI355X's 8 TB/s HBM peak; `traffic`
+carries the HBM bytes per launch that rocprofv3 counters measured for the same
+kernel source (profiles/), or null if the kernel changed since. `cpu_baseline`
+times the CPU oracle on a bounded slab of the same tensor.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+ROWS, COLS = 16384, 4096
+ALG_BYTES = ROWS * COLS * 2 + 2 * (ROWS * COLS + ROWS * COLS // 32)   # 272,629,760
+HBM_PEAK_GBS = 8000.0
+METRIC = "GB/s (read+write) and % of HBM peak, MXFP8 row+col cast 16384×4096"
+COUNTERS = os.path.join(ROOT, "profiles", "fused_cast_e4m3_16384x4096_counters.txt")
+KERNEL_SOURCES = ["microscaling_block_quantized_amd/csrc/mx_cast.hip",
+                  "microscaling_block_quantized_amd/csrc/mx_device.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x_gpu, budget_s: float = 12.0):
+    """The CPU oracle on consecutive 512-row slabs of the same tensor until the
+    time budget is used; GB/s on the same algorithmic-byte basis."""
+    import mx_inputs as I
+    import oracle as O
+    slab = 512
+    done_rows, t_used = 0, 0.0
+    while done_rows < ROWS and t_used < budget_s:
+        xs = I.to_bits(x_gpu[done_rows:done_rows + slab])
+        t0 = time.perf_counter()
+        O.quantize(xs, "bf16", O.E4M3, O.FLOOR, O.BOTH)
+        t_used += time.perf_counter() - t0
+        done_rows += slab
+    nbytes = ALG_BYTES * done_rows / ROWS
+    return {"value": round(nbytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done_rows} of {ROWS} rows ({done_rows * COLS} elements), fused row+col "
+                      f"E4M3 floor, NumPy float64 oracle, single thread, {t_used:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=3, help="rotating input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MX cast needs no "
+              "cross-GPU exchange, so run it once per GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import microscaling_block_quantized_amd as mx
+    import mx_inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xs, calls = [], []
+    for i in range(args.sets):
+        x = I.activations(ROWS, COLS, seed=1 + i, device=dev)
+        out = {
+            "row_codes": torch.empty((1, ROWS, COLS), dtype=torch.uint8, device=dev),
+            "row_scales": torch.empty((1, ROWS, COLS // 32), dtype=torch.uint8, device=dev),
+            "col_codes": torch.empty((1, COLS, ROWS), dtype=torch.uint8, device=dev),
+            "col_scales": torch.empty((1, COLS, ROWS // 32), dtype=torch.uint8, device=dev),
+        }
+        xs.append(x)
+        calls.append(mx.BoundQuantize(x, "e4m3", "floor", "both", out))
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        calls[i % args.sets]()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        calls[i % args.sets]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # a plain device copy of the same read+write byte count, as a measured ceiling
+    src = torch.empty(ALG_BYTES // 2, dtype=torch.uint8, device=dev)
+    dsts = [torch.empty_like(src) for _ in range(3)]
+    for d in dsts:
+        d.copy_(src)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(30):
+        dsts[i % 3].copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = ALG_BYTES / (c0.elapsed_time(c1) / 30 * 1e-3) / 1e9
+    del src, dsts
+
+    gbs = ALG_BYTES / (ms * 1e-3) / 1e9
+    traffic = read_counters()
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "activations 16384x4096 bf16 -> MXFP8 E4M3 row+col fused, floor scale rule",
+                   "rows": ROWS, "cols": COLS, "fmt": "e4m3", "scale_mode": "floor", "axis": "both",
+                   "buffer_sets": args.sets},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "copy_ceiling": {"value": round(copy_gbs, 2), "unit": "GB/s",
+                         "what": "torch device copy moving the same read+write bytes",
+                         "frac_of_ceiling": round(gbs / copy_gbs, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(xs[0])
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

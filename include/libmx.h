@@ -1,0 +1,115 @@
+/* libmx: OCP Microscaling (MX) block quantization on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("MXFP4 と NVFP4 は何が違うのか調べてみた", §2 MX family table and
+ * E8M0 paragraph, §4 "精度の差はどこから出るか"):
+ *   - a tensor is cut into blocks of 32 consecutive elements;
+ *   - each block gets one shared E8M0 scale: a power of two 2^e stored as the
+ *     byte e + 127 (codes 0..254 <-> 2^-127..2^127; 0xFF is NaN, no Inf);
+ *   - each element is stored as x / 2^e in the element format, MXFP8
+ *     (E4M3 or E5M2, 8.25 bits per element with the scale) or MXFP4 (E2M1,
+ *     two codes per byte, 4.25 bits per element), rounded to nearest-even
+ *     and clipped at the format's largest value;
+ *   - dequantization multiplies a code's value by its block's scale, an
+ *     exponent add with no rounding error (§7); a NaN scale makes the
+ *     whole block NaN (§2).
+ * The quantized data and the scales live in separate planes, one scale byte
+ * per 32 elements (§9, the Metal UE8M0 scale plane with 32x1 blocks).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are dense, row-major [batch][rows][cols]; cols is the
+ *     contiguous axis.
+ *   - Every data pointer is a device pointer allocated and owned by the
+ *     caller; libmx never allocates, frees or keeps memory, and keeps no
+ *     global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; nothing synchronizes inside libmx.
+ *     Device-side faults surface at the caller's next synchronization.
+ *   - Return value: MX_OK (0) or a negative MX_ERR_* code. Argument errors are
+ *     reported synchronously, before any HIP call. No exception crosses the ABI.
+ */
+#ifndef LIBMX_H
+#define LIBMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats. E4M3: bias 7, max 448, no Inf, NaN = S.1111.111.
+ * E5M2: bias 15, max 57344, IEEE Inf/NaN. E2M1: bias 1, values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, no Inf/NaN. */
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 } mx_fmt;
+
+/* Shared-exponent rules (same article, §4 and the rounding paragraph of §2):
+ * MX_SCALE_FLOOR   e = floor(log2(amax)) - emax (OCP example rule; the scaled
+ *                  block max lands in [2^emax, 2^(emax+1)), the excess clips);
+ * MX_SCALE_ROUNDUP the smallest e with amax <= max * 2^e (no clipping; the
+ *                  scaled block max lands in (max/2, max]).
+ * emax = floor(log2(max)): 8 (E4M3), 15 (E5M2), 2 (E2M1). e is clamped to
+ * [-127, 127]; an all-zero block gets code 0x00. A block holding a NaN or an
+ * Inf gets scale 0xFF and element codes 0x7F (FP8) or 0x0 (E2M1). */
+typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_ROUNDUP = 1 } mx_scale_mode;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
+
+/* Bitmask. ROW: blocks of 32 along cols. COL: blocks of 32 rows of one column,
+ * stored transposed (the column copy is the row-wise quantization of X^T). */
+typedef enum { MX_AXIS_ROW = 1, MX_AXIS_COL = 2, MX_AXIS_BOTH = 3 } mx_axis;
+
+typedef struct {
+  int64_t batch, rows, cols;
+} mx_shape;
+
+#define MX_OK 0
+#define MX_ERR_NULL (-1)        /* a required pointer is NULL, or an unused one is not */
+#define MX_ERR_SHAPE (-2)       /* non-positive extent, or a blocked extent % 32 != 0 */
+#define MX_ERR_ALIGN (-3)       /* x, codes or y not 16-byte aligned */
+#define MX_ERR_ENUM (-4)        /* unknown fmt / mode / dtype / axis */
+#define MX_ERR_ALIAS (-5)       /* input and an output overlap, or two outputs do */
+#define MX_ERR_TOO_LARGE (-6)   /* a size beyond what one launch can index */
+#define MX_ERR_LAUNCH (-7)      /* the kernel launch failed (hipGetLastError) */
+
+/* Bytes of ONE code plane and ONE scale plane for a tensor of shape s quantized
+ * to fmt (both axes have the same sizes): code = batch*rows*cols*bits/8,
+ * scale = batch*rows*cols/32. Shape rules are those of mx_quantize with
+ * MX_AXIS_BOTH. Pure host arithmetic; no HIP call. */
+int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_bytes);
+
+/* Quantize x ([batch][rows][cols], x_dtype) into the planes selected by axis.
+ *   row_codes  [batch][rows][cols] bytes, E2M1: [batch][rows][cols/2] with
+ *              element 2k in bits 3:0 and element 2k+1 in bits 7:4
+ *   row_scales [batch][rows][cols/32] E8M0 bytes
+ *   col_codes  [batch][cols][rows] bytes, E2M1: [batch][cols][rows/2]
+ *   col_scales [batch][cols][rows/32]
+ * Pointers of an axis not in `axis` must be NULL; the others must be non-NULL.
+ * Shape: batch, rows, cols >= 1; cols % 32 == 0 always (16-byte vector rows);
+ * rows % 32 == 0 when MX_AXIS_COL is set. x, row_codes and col_codes must be
+ * 16-byte aligned. Inputs and outputs must not overlap. */
+int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
+                mx_axis axis, void* row_codes, uint8_t* row_scales, void* col_codes,
+                uint8_t* col_scales, void* stream);
+
+/* Dequantize one plane. s is the shape of the plane as stored, with blocks of
+ * 32 along s.cols (a column plane is passed as [batch][cols][rows] and comes
+ * out as X^T). codes: batch*rows*cols bytes (E2M1: half); scales:
+ * batch*rows*cols/32 bytes; y: batch*rows*cols elements of y_dtype. FP32
+ * output is exact; BF16 output is the exact value rounded to nearest-even.
+ * NaN is written as 0x7FC00000 (FP32) / 0x7FC0 (BF16).
+ * Shape: extents >= 1, cols % 32 == 0. codes and y 16-byte aligned (E2M1
+ * codes 8-byte aligned). y must not overlap codes or scales. */
+int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s,
+                  mx_dtype y_dtype, void* y, void* stream);
+
+/* Static text for an MX_* code; never NULL. */
+const char* mx_strerror(int err);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMX_H */

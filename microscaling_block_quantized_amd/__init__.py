@@ -1,0 +1,193 @@
+"""Python binding of libmx (MX block quantization on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmx.so``. torch provides device memory and the current stream.
+The functions mirror the C ABI in ``include/libmx.h``:
+
+    mx_quantize(x, fmt, mode, axis)      -> dict of uint8 code / scale planes
+    mx_dequantize(codes, scales, fmt, shape, out_dtype)
+    mx_plane_bytes(fmt, shape)           -> (code bytes, scale bytes) of one plane
+    mx_strerror(err), mx_version()
+
+There is no CPU path: inputs must be GPU tensors, and a missing ``libmx.so``
+raises at the first call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MXError", "FMT", "MODE", "AXIS", "DTYPE", "lib_path", "load", "mx_version", "mx_strerror",
+    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize",
+]
+
+FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+MODE = {"floor": 0, "roundup": 1}
+AXIS = {"row": 1, "col": 2, "both": 3}
+DTYPE = {"f32": 0, "bf16": 1}
+EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_strerror", "mx_version")
+
+_LIB = None
+
+
+class MXError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: libmx error {code}: {mx_strerror(code)}")
+        self.code = code
+
+
+class MxShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmx.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmx.so (built by ``python -m microscaling_block_quantized_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmx.so not built at {path}; run "
+                           "`python -m microscaling_block_quantized_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u8p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    lib.mx_version.restype = i32
+    lib.mx_version.argtypes = []
+    lib.mx_strerror.restype = ctypes.c_char_p
+    lib.mx_strerror.argtypes = [i32]
+    lib.mx_plane_bytes.restype = i32
+    lib.mx_plane_bytes.argtypes = [i32, MxShape, ctypes.POINTER(ctypes.c_size_t),
+                                   ctypes.POINTER(ctypes.c_size_t)]
+    lib.mx_quantize.restype = i32
+    lib.mx_quantize.argtypes = [vp, i32, MxShape, i32, i32, i32, vp, u8p, vp, u8p, vp]
+    lib.mx_dequantize.restype = i32
+    lib.mx_dequantize.argtypes = [vp, u8p, i32, MxShape, i32, vp, vp]
+    _LIB = lib
+    return lib
+
+
+def mx_version() -> int:
+    return load().mx_version()
+
+
+def mx_strerror(err: int) -> str:
+    return load().mx_strerror(int(err)).decode()
+
+
+def _shape3(shape) -> tuple:
+    shape = tuple(int(v) for v in shape)
+    if len(shape) == 2:
+        return (1,) + shape
+    if len(shape) != 3:
+        raise ValueError(f"expected a 2-D or 3-D shape, got {shape}")
+    return shape
+
+
+def mx_plane_bytes(fmt: str, shape) -> tuple:
+    b, r, c = _shape3(shape)
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    err = load().mx_plane_bytes(FMT[fmt], MxShape(b, r, c), ctypes.byref(cb), ctypes.byref(sb))
+    if err:
+        raise MXError(err, "mx_plane_bytes")
+    return cb.value, sb.value
+
+
+def _stream_of(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+
+
+def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", out: dict | None = None):
+    """Quantize a GPU tensor [R][C] or [B][R][C] (bfloat16 or float32).
+
+    Returns {"row_codes", "row_scales"} and/or {"col_codes", "col_scales"} as
+    uint8 tensors: row planes [B][R][C'] / [B][R][C/32], column planes
+    [B][C][R'] / [B][C][R/32] (C' = C, or C/2 packed for e2m1); the batch axis
+    is dropped for a 2-D input. ``out`` may supply preallocated planes.
+    """
+    import torch
+    if not x.is_cuda:
+        raise ValueError("mx_quantize needs a GPU tensor (libmx has no CPU path)")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported input dtype {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous")
+    b, r, c = _shape3(x.shape)
+    squeeze = x.dim() == 2
+    ax = AXIS[axis]
+    div = 2 if fmt == "e2m1" else 1
+    out = out or {}
+    dev = x.device
+
+    def plane(name, shp):
+        t = out.get(name)
+        return t if t is not None else torch.empty(shp, dtype=torch.uint8, device=dev)
+
+    planes = {}
+    if ax & 1:
+        planes["row_codes"] = plane("row_codes", (b, r, c // div))
+        planes["row_scales"] = plane("row_scales", (b, r, c // 32))
+    if ax & 2:
+        planes["col_codes"] = plane("col_codes", (b, c, r // div))
+        planes["col_scales"] = plane("col_scales", (b, c, max(r // 32, 1)))
+    with torch.cuda.device(dev):
+        err = load().mx_quantize(
+            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
+            MODE[mode], ax, _ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")),
+            _ptr(planes.get("col_codes")), _ptr(planes.get("col_scales")), _stream_of(x))
+    if err:
+        raise MXError(err, "mx_quantize")
+    if squeeze:
+        planes = {k: v[0] for k, v in planes.items()}
+    return planes
+
+
+def mx_dequantize(codes, scales, fmt: str, shape, out_dtype: str = "f32", out=None):
+    """Dequantize one plane; ``shape`` is the element shape of the plane as stored
+    (blocks of 32 along its last axis). Returns a float32 or bfloat16 GPU tensor."""
+    import torch
+    if not codes.is_cuda or not scales.is_cuda:
+        raise ValueError("mx_dequantize needs GPU tensors (libmx has no CPU path)")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("codes and scales must be uint8")
+    if not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("codes and scales must be contiguous")
+    b, r, c = _shape3(shape)
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=codes.device)
+    with torch.cuda.device(codes.device):
+        err = load().mx_dequantize(_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c), DTYPE[out_dtype],
+                                   _ptr(y), _stream_of(codes))
+    if err:
+        raise MXError(err, "mx_dequantize")
+    return y
+
+
+class BoundQuantize:
+    """An mx_quantize call with its arguments marshalled once, for repeated
+    launches over fixed buffers (benchmark loops). Calling it enqueues one
+    quantize on the stream that was current at construction."""
+
+    def __init__(self, x, fmt: str, mode: str, axis: str, out: dict):
+        import torch
+        b, r, c = _shape3(x.shape)
+        self._fn = load().mx_quantize
+        self._args = (
+            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
+            MODE[mode], AXIS[axis], _ptr(out.get("row_codes")), _ptr(out.get("row_scales")),
+            _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _stream_of(x))
+        self._keep = (x, out)
+
+    def __call__(self) -> None:
+        err = self._fn(*self._args)
+        if err:
+            raise MXError(err, "mx_quantize")

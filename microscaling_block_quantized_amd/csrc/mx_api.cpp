@@ -1,0 +1,141 @@
+// C ABI of libmx: argument validation, plane-size arithmetic and kernel dispatch.
+// Every argument check runs before the first HIP call, so argument errors are
+// reported synchronously and without touching a device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/libmx.h"
+#include "mx_kernels.h"
+
+namespace {
+
+constexpr int64_t kBlock = 32;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+bool valid_fmt(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
+bool valid_mode(int m) { return m == MX_SCALE_FLOOR || m == MX_SCALE_ROUNDUP; }
+bool valid_dtype(int d) { return d == MX_F32 || d == MX_BF16; }
+bool valid_axis(int a) { return a == MX_AXIS_ROW || a == MX_AXIS_COL || a == MX_AXIS_BOTH; }
+
+int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : 8; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + uintptr_t(bytes)};
+}
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Element count, or -1 if an extent is non-positive or the product overflows.
+int64_t elements(const mx_shape& s) {
+  if (s.batch < 1 || s.rows < 1 || s.cols < 1) return -1;
+  const int64_t lim = INT64_C(1) << 56;
+  if (s.batch > lim || s.rows > lim || s.cols > lim) return -1;
+  if (s.rows > lim / s.cols) return -1;
+  const int64_t rc = s.rows * s.cols;
+  if (s.batch > lim / rc) return -1;
+  return s.batch * rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_version(void) { return 10000; }
+
+const char* mx_strerror(int err) {
+  switch (err) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL, or a pointer of an unused axis is not";
+    case MX_ERR_SHAPE: return "invalid shape: extents must be >= 1 and blocked extents multiples of 32";
+    case MX_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case MX_ERR_ENUM: return "unknown format, scale mode, dtype or axis";
+    case MX_ERR_ALIAS: return "input and output buffers overlap";
+    case MX_ERR_TOO_LARGE: return "tensor too large for one launch";
+    case MX_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown libmx error";
+  }
+}
+
+int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_bytes) {
+  if (!valid_fmt(fmt)) return MX_ERR_ENUM;
+  if (code_bytes == nullptr || scale_bytes == nullptr) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
+  *code_bytes = size_t(n / 8 * code_bits(fmt));
+  *scale_bytes = size_t(n / kBlock);
+  return MX_OK;
+}
+
+int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
+                mx_axis axis, void* row_codes, uint8_t* row_scales, void* col_codes,
+                uint8_t* col_scales, void* stream) {
+  if (!valid_fmt(fmt) || !valid_mode(mode) || !valid_dtype(x_dtype) || !valid_axis(axis))
+    return MX_ERR_ENUM;
+  const bool want_row = (axis & MX_AXIS_ROW) != 0;
+  const bool want_col = (axis & MX_AXIS_COL) != 0;
+  if (x == nullptr) return MX_ERR_NULL;
+  if (want_row != (row_codes != nullptr) || want_row != (row_scales != nullptr)) return MX_ERR_NULL;
+  if (want_col != (col_codes != nullptr) || want_col != (col_scales != nullptr)) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
+  if (want_col && s.rows % kBlock != 0) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || (want_row && !aligned(row_codes, 16)) || (want_col && !aligned(col_codes, 16)))
+    return MX_ERR_ALIGN;
+
+  const int64_t in_bytes = n * (x_dtype == MX_BF16 ? 2 : 4);
+  const int64_t cbytes = n / 8 * code_bits(fmt);
+  const int64_t sbytes = n / kBlock;
+  Range rs[5];
+  int nr = 0;
+  rs[nr++] = range_of(x, in_bytes);
+  if (want_row) { rs[nr++] = range_of(row_codes, cbytes); rs[nr++] = range_of(row_scales, sbytes); }
+  if (want_col) { rs[nr++] = range_of(col_codes, cbytes); rs[nr++] = range_of(col_scales, sbytes); }
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
+
+  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols);
+  if (g.blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
+
+  mx::CastArgs a;
+  a.x = x;
+  a.row_codes = row_codes;
+  a.row_scales = row_scales;
+  a.col_codes = col_codes;
+  a.col_scales = col_scales;
+  a.rows = s.rows;
+  a.cols = s.cols;
+  a.tiles_r = uint32_t(g.tiles_r);
+  a.tiles_c = uint32_t(g.tiles_c);
+  const hipError_t e = mx::launch_cast(x_dtype == MX_BF16, int(fmt), int(mode), int(axis), a,
+                                       uint32_t(g.blocks), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s,
+                  mx_dtype y_dtype, void* y, void* stream) {
+  if (!valid_fmt(fmt) || !valid_dtype(y_dtype)) return MX_ERR_ENUM;
+  if (codes == nullptr || scales == nullptr || y == nullptr) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
+  if (!aligned(codes, fmt == MX_E2M1 ? 8 : 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
+  const Range rc = range_of(codes, n / 8 * code_bits(fmt));
+  const Range rsc = range_of(scales, n / kBlock);
+  const Range ry = range_of(y, n * (y_dtype == MX_BF16 ? 2 : 4));
+  if (overlap(ry, rc) || overlap(ry, rsc)) return MX_ERR_ALIAS;
+  if ((n / 16 + 255) / 256 > kMaxGrid) return MX_ERR_TOO_LARGE;
+  const hipError_t e = mx::launch_dequant(int(fmt), y_dtype == MX_BF16, static_cast<const uint8_t*>(codes),
+                                          scales, y, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+}  // extern "C"

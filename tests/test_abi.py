@@ -1,0 +1,119 @@
+"""The C ABI on the host: exported symbols, plane sizes and argument errors.
+
+None of these calls reaches a GPU: every error path returns before the first
+HIP call, and only error paths are exercised here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import microscaling_block_quantized_amd as mxb
+from microscaling_block_quantized_amd import MxShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "libmx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mx_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mxb.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert names == sorted(mxb.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert mxb.mx_version() == 10000
+    for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
+        s = mxb.mx_strerror(code)
+        assert isinstance(s, str) and s
+    assert mxb.mx_strerror(-99) == "unknown libmx error"
+
+
+@pytest.mark.parametrize("fmt,bpe", [("e4m3", 8.25), ("e5m2", 8.25), ("e2m1", 4.25)])
+def test_plane_bytes(fmt, bpe):
+    # "MXFP4 と NVFP4 は何が違うのか調べてみた" §2: 4.25 / 8.25 bits per element
+    for shape in [(16384, 4096), (14336, 4096), (64, 4096, 14336), (1, 32)]:
+        cb, sb = mxb.mx_plane_bytes(fmt, shape)
+        n = 1
+        for v in shape:
+            n *= v
+        assert (cb + sb) * 8 / n == bpe
+        assert sb == n // 32
+
+
+def test_plane_bytes_errors(lib):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.mx_plane_bytes(0, MxShape(1, 4, 33), ctypes.byref(cb), ctypes.byref(sb)) == E_SHAPE
+    assert lib.mx_plane_bytes(0, MxShape(0, 4, 32), ctypes.byref(cb), ctypes.byref(sb)) == E_SHAPE
+    assert lib.mx_plane_bytes(7, MxShape(1, 4, 32), ctypes.byref(cb), ctypes.byref(sb)) == E_ENUM
+    assert lib.mx_plane_bytes(0, MxShape(1, 4, 32), None, ctypes.byref(sb)) == E_NULL
+
+
+# Fake, well-aligned, non-overlapping addresses: never dereferenced, because
+# every call below fails validation first.
+X, RC, RS, CC, CS, Y = (0x10000000 * k for k in range(1, 7))
+
+
+def q(lib, x=X, dt=1, shape=(1, 64, 64), fmt=0, mode=0, axis=3, rc=RC, rs=RS, cc=CC, cs=CS):
+    v = lambda p: ctypes.c_void_p(p)
+    return lib.mx_quantize(v(x), dt, MxShape(*shape), fmt, mode, axis, v(rc), v(rs), v(cc), v(cs), None)
+
+
+def test_quantize_argument_errors(lib):
+    assert q(lib, fmt=3) == E_ENUM
+    assert q(lib, mode=2) == E_ENUM
+    assert q(lib, dt=2) == E_ENUM
+    assert q(lib, axis=0) == E_ENUM
+    assert q(lib, axis=4) == E_ENUM
+    assert q(lib, x=0) == E_NULL
+    assert q(lib, rc=0) == E_NULL
+    assert q(lib, cs=0) == E_NULL
+    assert q(lib, axis=1) == E_NULL                    # column pointers must be NULL for row-only
+    assert q(lib, axis=1, cc=0, cs=0, shape=(1, 64, 48)) == E_SHAPE
+    assert q(lib, shape=(1, 48, 64)) == E_SHAPE        # column blocks need rows % 32 == 0
+    assert q(lib, shape=(0, 64, 64)) == E_SHAPE
+    assert q(lib, shape=(1, -32, 64)) == E_SHAPE
+    assert q(lib, shape=(1, 1 << 40, 1 << 40)) == E_SHAPE
+    assert q(lib, x=X + 8) == E_ALIGN
+    assert q(lib, rc=RC + 4) == E_ALIGN
+    assert q(lib, cc=CC + 1) == E_ALIGN
+    assert q(lib, rc=X + 1024) == E_ALIAS              # row codes inside the input
+    assert q(lib, cs=RS) == E_ALIAS                    # two outputs on one buffer
+
+
+def test_dequantize_argument_errors(lib):
+    v = lambda p: ctypes.c_void_p(p)
+    dq = lambda c=CC, s=CS, fmt=0, shape=(1, 64, 64), dt=0, y=Y: lib.mx_dequantize(
+        v(c), v(s), fmt, MxShape(*shape), dt, v(y), None)
+    assert dq(fmt=9) == E_ENUM
+    assert dq(dt=5) == E_ENUM
+    assert dq(c=0) == E_NULL
+    assert dq(s=0) == E_NULL
+    assert dq(y=0) == E_NULL
+    assert dq(shape=(1, 64, 40)) == E_SHAPE
+    assert dq(shape=(1, 0, 64)) == E_SHAPE
+    assert dq(c=CC + 8) == E_ALIGN
+    assert dq(y=Y + 4) == E_ALIGN
+    assert dq(y=CC + 16) == E_ALIAS
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        mxb.mx_quantize(torch.zeros(32, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        mxb.mx_dequantize(torch.zeros(32, dtype=torch.uint8), torch.zeros(1, dtype=torch.uint8), "e4m3", (1, 32))

@@ -1,0 +1,93 @@
+"""C ABI behaviour on the GPU: streams, guard bands around outputs, reuse of
+output buffers, and errors that only a real device can reach."""
+import numpy as np
+import pytest
+import torch
+
+import mx_inputs as I
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+CANARY = 0xA5
+
+
+def guarded(nbytes):
+    buf = torch.full((nbytes + 2 * GUARD,), CANARY, dtype=torch.uint8, device="cuda")
+    return buf, buf[GUARD:GUARD + nbytes]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("shape", [(160, 96), (2, 96, 224), (1, 33, 64)])
+def test_writes_stay_inside_outputs(mx, fmt, shape):
+    """Every output plane sits between 4 KiB canary bands that must survive."""
+    x = torch.randn(shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    b, r, c = (1,) + tuple(shape) if len(shape) == 2 else shape
+    axis = "both" if r % 32 == 0 else "row"
+    div = 2 if fmt == "e2m1" else 1
+    sizes = {"row_codes": (b, r, c // div), "row_scales": (b, r, c // 32),
+             "col_codes": (b, c, r // div), "col_scales": (b, c, max(r // 32, 1))}
+    keys = ["row_codes", "row_scales"] + (["col_codes", "col_scales"] if axis == "both" else [])
+    bufs, out = {}, {}
+    for k in keys:
+        n = int(np.prod(sizes[k]))
+        bufs[k], view = guarded(n)
+        out[k] = view.view(sizes[k])
+    mx.mx_quantize(x.view(b, r, c), fmt, "floor", axis, out=out)
+    torch.cuda.synchronize()
+    ref = O.quantize(I.to_bits(x.view(b, r, c).cpu()), "bf16", {"e4m3": O.E4M3, "e2m1": O.E2M1}[fmt],
+                     O.FLOOR, O.BOTH if axis == "both" else O.ROW)
+    for k in keys:
+        buf = bufs[k].cpu().numpy()
+        assert (buf[:GUARD] == CANARY).all() and (buf[-GUARD:] == CANARY).all(), k
+        assert np.array_equal(out[k].cpu().numpy(), ref[k]), k
+
+
+def test_dequant_writes_stay_inside_output(mx):
+    codes = torch.randint(0, 256, (96, 64), dtype=torch.uint8, generator=torch.Generator().manual_seed(1)).cuda()
+    scales = torch.full((96, 2), 120, dtype=torch.uint8, device="cuda")
+    buf, view = guarded(96 * 64 * 2)
+    y = view.view(torch.bfloat16).view(96, 64)
+    mx.mx_dequantize(codes, scales, "e4m3", (96, 64), "bf16", out=y)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert (b[:GUARD] == CANARY).all() and (b[-GUARD:] == CANARY).all()
+
+
+def test_runs_on_the_callers_stream(mx):
+    x = I.activations(512, 256, seed=3, device="cuda")
+    ref = mx.mx_quantize(x, "e4m3", "floor", "both")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # the work is enqueued on s; the result is only read after s is synchronized
+        out = mx.mx_quantize(x, "e4m3", "floor", "both")
+    s.synchronize()
+    for k in ref:
+        assert torch.equal(ref[k], out[k]), k
+
+
+def test_output_buffers_can_be_reused(mx):
+    a = I.activations(256, 256, seed=4, device="cuda")
+    b = I.activations(256, 256, seed=5, device="cuda")
+    out = mx.mx_quantize(a, "e5m2", "roundup", "both")
+    first = {k: v.clone() for k, v in out.items()}
+    mx.mx_quantize(b, "e5m2", "roundup", "both", out=out)
+    fresh = mx.mx_quantize(b, "e5m2", "roundup", "both")
+    torch.cuda.synchronize()
+    for k in out:
+        assert torch.equal(out[k], fresh[k])
+    assert any(not torch.equal(first[k], out[k]) for k in out)
+
+
+def test_device_argument_errors(mx):
+    x = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize(x[:, :48].contiguous(), "e4m3", "floor", "row")
+    assert e.value.code == -2
+    raw = torch.zeros(64 * 64 + 16, dtype=torch.uint8, device="cuda")
+    misaligned = raw[1:1 + 64 * 64].view(64, 64)         # one byte past a 16-byte boundary
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize(x, "e4m3", "floor", "row", out={"row_codes": misaligned})
+    assert e.value.code == -3

@@ -1,0 +1,271 @@
+"""Bit-exact parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Codes and scales must match exactly; dequantized outputs must match bit for
+bit (NaN is canonical on both sides). Inputs come from mx_inputs only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_inputs as I
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+OFMT = {"e4m3": O.E4M3, "e5m2": O.E5M2, "e2m1": O.E2M1}
+OMODE = {"floor": O.FLOOR, "roundup": O.ROUNDUP}
+OAXIS = {"row": O.ROW, "col": O.COL, "both": O.BOTH}
+FMTS = ["e4m3", "e5m2", "e2m1"]
+MODES = ["floor", "roundup"]
+
+
+def gpu_quant(mx, x, fmt, mode, axis):
+    out = mx.mx_quantize(x.cuda().contiguous(), fmt, mode, axis)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def oracle_quant(x, fmt, mode, axis):
+    dt = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    out = O.quantize(I.to_bits(x), dt, OFMT[fmt], OMODE[mode], OAXIS[axis])
+    if x.dim() == 2:
+        out = {k: v[0] for k, v in out.items()}
+    return out
+
+
+def assert_same(got, exp, what=""):
+    assert set(got) == set(exp), (got.keys(), exp.keys())
+    for k in exp:
+        g, e = got[k], exp[k]
+        assert g.shape == e.shape, (what, k, g.shape, e.shape)
+        bad = np.argwhere(g != e)
+        if bad.size:
+            idx = tuple(bad[0])
+            raise AssertionError(f"{what} {k}: {len(bad)} mismatches, first at {idx}: "
+                                 f"gpu={g[idx]:#x} oracle={e[idx]:#x}")
+
+
+def check(mx, x, fmt, mode, axis, what=""):
+    assert_same(gpu_quant(mx, x, fmt, mode, axis), oracle_quant(x, fmt, mode, axis), what)
+
+
+def pad_rows(t, mult=32):
+    pad = (-t.shape[0]) % mult
+    if pad:
+        t = torch.cat([t, torch.zeros((pad,) + tuple(t.shape[1:]), dtype=t.dtype)])
+    return t
+
+
+# ---------------- exhaustive and directed inputs ----------------
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_bf16_sweep_rows(mx, fmt, mode):
+    """Every BF16 pattern under every reachable shared scale, blocks along rows."""
+    check(mx, I.bf16_sweep(fmt), fmt, mode, "row", "sweep/row")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_bf16_sweep_columns(mx, fmt, mode):
+    """The same sweep with each block laid down a column (fused kernel, both planes)."""
+    x = pad_rows(I.bf16_sweep(fmt)).T.contiguous()          # [32, n]
+    check(mx, x, fmt, mode, "both", "sweep/col")
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_bf16_amax_sweep(mx, fmt, mode, axis):
+    x = pad_rows(I.bf16_amax_sweep())
+    if axis == "col":
+        x = x.T.contiguous()
+    check(mx, x, fmt, mode, axis, "amax")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_edge_blocks(mx, fmt, mode, dt):
+    x = I.fp32_edges(fmt) if dt == "f32" else I.bf16_edges(fmt)
+    x = pad_rows(x)
+    check(mx, x, fmt, mode, "row", "edges/row")
+    check(mx, x.T.contiguous(), fmt, mode, "both", "edges/col")
+
+
+# ---------------- workloads at small sizes (several tiles + ragged tails) ----------------
+
+def test_fp32_normal_quant_dequant(mx):
+    """256x1024 FP32 N(0,1), row-wise E4M3, floor rule, then dequantize to FP32."""
+    x = I.fp32_normal(256, 1024, seed=0)
+    got = gpu_quant(mx, x, "e4m3", "floor", "row")
+    exp = oracle_quant(x, "e4m3", "floor", "row")
+    assert_same(got, exp, "fp32_normal")
+    rc = torch.from_numpy(got["row_codes"]).cuda()
+    rs = torch.from_numpy(got["row_scales"]).cuda()
+    y = mx.mx_dequantize(rc, rs, "e4m3", (256, 1024), "f32")
+    torch.cuda.synchronize()
+    ref = O.dequantize(exp["row_codes"], exp["row_scales"], O.E4M3, "f32")
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref)
+
+
+@pytest.mark.parametrize("shape", [(544, 416), (128, 128), (32, 32), (96, 4128)])
+def test_activations_fused(mx, shape):
+    check(mx, I.activations(*shape, seed=11), "e4m3", "floor", "both", f"act{shape}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_weights_e2m1(mx, mode):
+    x = I.weights(352, 288, seed=12)
+    check(mx, x, "e2m1", mode, "row", "weights")
+    check(mx, x, "e2m1", mode, "both", "weights/both")
+
+
+@pytest.mark.parametrize("axis", ["col", "both"])
+def test_gradients_e5m2(mx, axis):
+    x = I.gradients(288, 352, seed=13)
+    assert torch.isnan(x).any() or torch.isinf(x).any()
+    check(mx, x, "e5m2", "roundup", axis, "grads")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_wide_range_batch_round_trip(mx, out_dtype):
+    b, r, c = 3, 160, 288
+    x = torch.stack([I.wide_range(i, r, c, seed=14) for i in range(b)])
+    got = gpu_quant(mx, x, "e4m3", "floor", "both")
+    exp = oracle_quant(x, "e4m3", "floor", "both")
+    assert_same(got, exp, "wide")
+    for plane, shp in (("row", (b, r, c)), ("col", (b, c, r))):
+        codes = torch.from_numpy(got[f"{plane}_codes"]).cuda()
+        scales = torch.from_numpy(got[f"{plane}_scales"]).cuda()
+        y = mx.mx_dequantize(codes, scales, "e4m3", shp, out_dtype)
+        torch.cuda.synchronize()
+        ref = O.dequantize(exp[f"{plane}_codes"], exp[f"{plane}_scales"], O.E4M3, out_dtype)
+        yb = y.cpu().contiguous()
+        yb = yb.view(torch.int16).numpy().view(np.uint16) if out_dtype == "bf16" else yb.numpy().view(np.uint32)
+        assert np.array_equal(yb, ref), plane
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_ragged_shapes(mx, fmt, dt):
+    g = torch.Generator().manual_seed(21)
+    shapes = [(1, 33, 32, "row"), (2, 64, 160, "both"), (1, 32, 32, "col"), (3, 96, 224, "both"),
+              (1, 1, 4096, "row"), (2, 160, 96, "col"), (1, 257, 64, "row")]
+    for b, r, c, axis in shapes:
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-8, 8, (b, r, 1), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
+        for mode in MODES:
+            check(mx, x, fmt, mode, axis, f"ragged {(b, r, c, axis, mode)}")
+
+
+# ---------------- dequantization ----------------
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_every_code_and_scale(mx, fmt, out_dtype):
+    """Every element code under every scale code 0..255, each in its own block."""
+    ncode = 1 << OFMT[fmt].bits
+    codes = np.tile(np.arange(ncode, dtype=np.uint8), 256)
+    scales = np.repeat(np.arange(256, dtype=np.uint8), ncode)
+    blocks = np.zeros((codes.size, 32), dtype=np.uint8)
+    blocks[:, :] = codes[:, None]                         # whole block holds the code
+    packed = O.pack_e2m1(blocks) if fmt == "e2m1" else blocks
+    sc = scales.reshape(-1, 1)
+    y = mx.mx_dequantize(torch.from_numpy(np.ascontiguousarray(packed)).cuda(), torch.from_numpy(sc).cuda(),
+                         fmt, (blocks.shape[0], 32), out_dtype)
+    torch.cuda.synchronize()
+    ref = O.dequantize(packed, sc, OFMT[fmt], out_dtype)
+    yb = y.cpu()
+    yb = yb.view(torch.int16).numpy().view(np.uint16) if out_dtype == "bf16" else yb.numpy().view(np.uint32)
+    bad = np.argwhere(yb != ref)
+    assert bad.size == 0, (bad[:3], blocks[bad[0][0], 0], sc[bad[0][0]], yb[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+# ---------------- full-size workloads, sampled against the oracle ----------------
+
+def slab_check(mx_out, x_slab_cpu, r0, fmt, mode, axis, batch_index=None):
+    """Compare the rows r0..r0+n of the GPU planes with the oracle on that slab."""
+    n = x_slab_cpu.shape[0]
+    exp = oracle_quant(x_slab_cpu, fmt, mode, axis)
+    div = 2 if fmt == "e2m1" else 1
+    for k, e in exp.items():
+        t = mx_out[k] if batch_index is None else mx_out[k][batch_index]
+        if k == "row_codes":
+            g = t[r0:r0 + n]
+        elif k == "row_scales":
+            g = t[r0:r0 + n]
+        elif k == "col_codes":
+            g = t[:, r0 // div:(r0 + n) // div]
+        else:
+            g = t[:, r0 // 32:(r0 + n) // 32]
+        g = g.cpu().numpy()
+        bad = np.argwhere(g != e)
+        assert bad.size == 0, (k, r0, bad[:3])
+
+
+def test_full_activations_fused(mx):
+    """16384x4096 BF16 activations, fused row+column E4M3 (floor), sampled slabs."""
+    x = I.activations(16384, 4096, seed=1, device="cuda")
+    out = mx.mx_quantize(x, "e4m3", "floor", "both")
+    torch.cuda.synchronize()
+    for r0 in (0, 8192 - 128, 16384 - 256):
+        slab_check(out, x[r0:r0 + 256].cpu(), r0, "e4m3", "floor", "both")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_full_weights_e2m1(mx, mode):
+    x = I.weights(14336, 4096, seed=2, device="cuda")
+    out = mx.mx_quantize(x, "e2m1", mode, "row")
+    torch.cuda.synchronize()
+    for r0 in (0, 7000, 14336 - 256):
+        slab_check(out, x[r0:r0 + 256].cpu(), r0, "e2m1", mode, "row")
+
+
+def test_full_gradients_e5m2_col(mx):
+    x = I.gradients(8192, 8192, seed=3, device="cuda")
+    out = mx.mx_quantize(x, "e5m2", "roundup", "col")
+    torch.cuda.synchronize()
+    for r0 in (0, 4096, 8192 - 256):
+        slab_check(out, x[r0:r0 + 256].cpu(), r0, "e5m2", "roundup", "col")
+    # specials are present at full size and every one of their column blocks is NaN-scaled
+    bad = (~torch.isfinite(x)).nonzero()
+    sc = out["col_scales"]
+    assert bad.shape[0] > 0
+    assert (sc[bad[:, 1], bad[:, 0] // 32] == 0xFF).all()
+
+
+def test_full_wide_range_pipeline(mx):
+    """64 x 4096x14336 BF16: fused E4M3 quantize, then both planes dequantized to
+    BF16. Two tensors are sampled against the oracle; the rest are checked
+    through properties that hold at any size."""
+    B, R, C = 64, 4096, 14336
+    x = I.wide_range_batch(B, R, C, seed=4, device="cuda")
+    out = mx.mx_quantize(x, "e4m3", "floor", "both")
+    yr = mx.mx_dequantize(out["row_codes"], out["row_scales"], "e4m3", (B, R, C), "bf16")
+    yc = mx.mx_dequantize(out["col_codes"], out["col_scales"], "e4m3", (B, C, R), "bf16")
+    torch.cuda.synchronize()
+    for bi in (0, B - 1):
+        r0 = 1024
+        xs = x[bi, r0:r0 + 256].cpu()
+        slab_check(out, xs, r0, "e4m3", "floor", "both", batch_index=bi)
+        exp = oracle_quant(xs, "e4m3", "floor", "both")
+        ref_r = O.dequantize(exp["row_codes"], exp["row_scales"], O.E4M3, "bf16")
+        ref_c = O.dequantize(exp["col_codes"], exp["col_scales"], O.E4M3, "bf16")
+        got_r = yr[bi, r0:r0 + 256].cpu().view(torch.int16).numpy().view(np.uint16)
+        got_c = yc[bi, :, r0:r0 + 256].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got_r, ref_r)
+        assert np.array_equal(got_c, ref_c)
+    # at full size: round-trip error bound of E4M3 under the floor rule. The
+    # largest magnitude of a block maps into [256, 512); elements whose scaled
+    # magnitude is in the normal range keep a relative error <= 2^-4, clipped
+    # ones lie within [448, 512) * 2^e, and the rest are within half the
+    # subnormal step 2^-10 * 2^e of x.
+    for bi in range(0, B, 9):
+        xf = x[bi].float()
+        e = out["row_scales"][bi].to(torch.int32) - 127
+        step = torch.exp2(e.float() - 10).repeat_interleave(32, dim=1)
+        err = (yr[bi].float() - xf).abs()
+        rel_ok = err <= xf.abs() * 2.0 ** -4 + step
+        clip_ok = xf.abs() >= 448.0 * step * 1024
+        assert bool((rel_ok | clip_ok).all()), bi
