@@ -62,6 +62,75 @@ def read_counters():
         return None
 
 
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = ALG_BYTES // 2          # each timed torch copy reads and writes this many bytes
+CAST_KERNEL = "mx_cast_kernel<true, 0, 0, 3>"
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(stats_csv: str, command: str) -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv)."""
+    out = ["# rocprofv3 kernel trace: fused MXFP8 E4M3 row+col cast, 16384x4096 BF16", "",
+           f"command: {command}", "", "| kernel | calls | average us | min us | max us | algorithmic GB/s |",
+           "|---|---|---|---|---|---|"]
+    for r in _csv_rows(stats_csv):
+        name = r["Name"]
+        short = "mx_cast_kernel<bf16,E4M3,floor,row+col>" if CAST_KERNEL in name else (
+            "torch device copy (" + COPY_KERNEL + ")" if COPY_KERNEL in name else None)
+        if short is None:
+            continue
+        avg = float(r["AverageNs"]) / 1e3
+        nbytes = ALG_BYTES if CAST_KERNEL in name else 2 * COPY_BYTES
+        out.append(f"| {short} | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{float(r['MaxNs']) / 1e3:.2f} | {nbytes / (avg * 1e-6) / 1e9:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
+    """HBM bytes per launch of the cast from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for torch's copy kernel
+    moving a known number of bytes in the same run."""
+    def per_kernel(path, counter):
+        acc = {}
+        for r in _csv_rows(path):
+            if r["Counter_Name"] != counter:
+                continue
+            key = "cast" if CAST_KERNEL in r["Kernel_Name"] else ("copy" if COPY_KERNEL in r["Kernel_Name"] else None)
+            if key:
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    f_cal = COPY_BYTES / (f["copy"] * 1024.0)
+    w_cal = COPY_BYTES / (w["copy"] * 1024.0)
+    fetch_b = f["cast"] * 1024.0 * f_cal
+    write_b = w["cast"] * 1024.0 * w_cal
+    alg_read = ROWS * COLS * 2
+    alg_write = ALG_BYTES - alg_read
+    lines = [
+        "# rocprofv3 HBM counters: fused MXFP8 E4M3 row+col cast, 16384x4096 BF16",
+        "",
+        f"command (FETCH_SIZE): {command.format(counter='FETCH_SIZE')}",
+        f"command (WRITE_SIZE): {command.format(counter='WRITE_SIZE')}",
+        "",
+        f"calibration: torch copy kernel {COPY_KERNEL} moving {COPY_BYTES} B each way reads "
+        f"FETCH_SIZE {f['copy']:.1f} KiB (factor {f_cal:.4f}) and WRITE_SIZE {w['copy']:.1f} KiB (factor {w_cal:.4f})",
+        f"cast raw: FETCH_SIZE {f['cast']:.1f} KiB, WRITE_SIZE {w['cast']:.1f} KiB per dispatch",
+        f"cast fetched bytes per launch (calibrated): {fetch_b:.0f}  (algorithmic read {alg_read}, "
+        f"ratio {fetch_b / alg_read:.4f})",
+        f"cast written bytes per launch (calibrated): {write_b:.0f}  (algorithmic write {alg_write}, "
+        f"ratio {write_b / alg_write:.4f})",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"kernel_source_hash: {kernel_hash()}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(x_gpu, budget_s: float = 12.0):
     """The CPU oracle on consecutive 512-row slabs of the same tensor until the
     time budget is used; GB/s on the same algorithmic-byte basis."""
@@ -88,7 +157,18 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3, help="rotating input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the calibrated HBM-traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.command), end="")
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.command), end="")
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MX cast needs no "
               "cross-GPU exchange, so run it once per GPU.", file=sys.stderr)

@@ -68,7 +68,8 @@ typedef struct {
 #define MX_ERR_ALIGN (-3)       /* x, codes or y not 16-byte aligned */
 #define MX_ERR_ENUM (-4)        /* unknown fmt / mode / dtype / axis */
 #define MX_ERR_ALIAS (-5)       /* input and an output overlap, or two outputs do */
-#define MX_ERR_TOO_LARGE (-6)   /* a size beyond what one launch can index */
+#define MX_ERR_TOO_LARGE (-6)   /* beyond one launch: cols >= 2^22, rows >= 2^23 with
+                                   column planes, or more than 2^31-1 tiles */
 #define MX_ERR_LAUNCH (-7)      /* the kernel launch failed (hipGetLastError) */
 
 /* Bytes of ONE code plane and ONE scale plane for a tensor of shape s quantized

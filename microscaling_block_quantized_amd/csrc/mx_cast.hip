@@ -8,231 +8,270 @@
 // column blocks are 32 rows of one column and are written transposed, so the
 // column copy is the row-wise quantization of X^T.
 //
-// One workgroup (4 waves) owns a 128-row x 128-column tile of one batch
-// slice and reads it from HBM exactly once:
-//   * lane = q * LPR + t: t picks a 16-byte column chunk (8 BF16 / 4 FP32),
-//     q a group of RPT consecutive rows; wave w owns rows 32w .. 32w+31, so
-//     one wave holds exactly one 32-row column block of the tile.
+// Work decomposition (gfx950, 64-wide waves). A workgroup of 8 waves owns a
+// 128-row x 256-column tile of one batch slice and reads it from HBM once:
+//   * wave w = 4 * wc + wr covers rows 32*wr .. +31 and columns 128*wc .. +127;
+//     lane = q * LPR + t, where t picks a 16-byte chunk of a row (8 BF16 or
+//     4 FP32 elements) and q a group of RPT consecutive rows. One wave thus
+//     holds exactly one 32-row column block for each of its 128 columns.
 //   * row blocks: lane-local max, then a max over the 4 (BF16) or 8 (FP32)
-//     lanes that share the block; codes go straight to HBM, 128 contiguous
-//     bytes per row.
+//     lanes sharing the block; codes go straight to HBM, and the 4 scale bytes
+//     of a row's 128 columns are gathered into one dword store.
 //   * column blocks: in-lane max over the thread's RPT rows, then a max over
-//     the RG lanes that hold the other rows of the same 32-row block. The
-//     1-byte codes (not the inputs) are staged in LDS as [column][row] so the
-//     transposed plane is written in full 128-byte runs.
+//     the RG lanes holding the other rows of the block. The codes (1 byte, not
+//     the inputs) are staged in LDS as [column][row] with a 16-byte XOR swizzle
+//     and written out as 128-byte runs of the transposed plane.
+// Memory-system choices, all measured on MI355X for the 16384x4096 fused
+// cast: the input is read and the row codes are written with non-temporal
+// accesses, while the transposed column runs and the scale planes go through
+// L2 with ordinary stores (scale bytes of one 128-byte line come from several
+// workgroups and must merge in L2). Tiles are ordered so that each XCD owns a
+// strip of adjacent tile columns and sweeps down the rows.
 #include "mx_kernels.h"
 
 namespace mx {
 
 namespace {
 
-constexpr int kTileR = 128;
-constexpr int kTileC = 128;
-constexpr int kThreads = 256;
-constexpr int kPitch = 144;      // LDS bytes per staged column (128 codes + pad)
+constexpr int kWaveRows = 4;                 // waves stacked along rows (32 rows each)
+constexpr int kWaveCols = 2;                 // waves side by side along columns (128 each)
+constexpr int kTileR = 32 * kWaveRows;       // 128
+constexpr int kTileC = 128 * kWaveCols;      // 256
+constexpr int kThreads = 64 * kWaveRows * kWaveCols;
+constexpr int kXcds = 8;
 
-// Hardware places workgroup i on XCD i % 8. Renumber so that each XCD walks a
-// contiguous range of tiles; neighbouring tiles then share an L2.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nb) {
-  const uint32_t xcd = bid & 7u, idx = bid >> 3;
-  const uint32_t per = nb >> 3, rem = nb & 7u;
-  return xcd * per + min(xcd, rem) + idx;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt8(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt4(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
+  __builtin_nontemporal_store(static_cast<unsigned short>(v), reinterpret_cast<unsigned short*>(p));
+}
+
+// Workgroup i runs on XCD i % 8. Give XCD x the x-th contiguous eighth of a
+// tile sequence that is ordered strip-major: tile columns are cut into 8
+// strips, and each strip is walked batch by batch, row by row. Neighbouring
+// tiles of one strip then run at the same time on the same XCD.
+__device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nb, uint32_t tiles_r, uint32_t tiles_c,
+                                            uint32_t& b, uint32_t& tr, uint32_t& tc) {
+  const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
+  const uint32_t per = nb / kXcds, rem = nb % kXcds;
+  const uint32_t i = xcd * per + min(xcd, rem) + idx;                // position in the sequence
+  const uint32_t w = (tiles_c + kXcds - 1) / kXcds;                  // strip width in tiles
+  const uint32_t rows_total = nb / tiles_c;                          // batch * tiles_r
+  const uint32_t strip = i / (rows_total * w);
+  const uint32_t in = i - strip * rows_total * w;
+  const uint32_t ws = min(w, tiles_c - strip * w);
+  const uint32_t rowi = in / ws;
+  tc = strip * w + (in - rowi * ws);
+  b = rowi / tiles_r;
+  tr = rowi - b * tiles_r;
 }
 
 template <bool BF16, int F, int M, int AX>
-__global__ __launch_bounds__(kThreads) void mx_cast_kernel(CastArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 3))) void mx_cast_kernel(CastArgs a) {
   constexpr int VEC = InC<BF16>::vec;          // elements per 16-byte chunk
-  constexpr int LPR = kTileC / VEC;            // lanes per tile row: 16 | 32
+  constexpr int ES = BF16 ? 2 : 4;             // input element bytes
+  constexpr int LPR = 128 / VEC;               // lanes per 128-column wave row: 16 | 32
   constexpr int RG = 64 / LPR;                 // row groups per wave: 4 | 2
   constexpr int RPT = 32 / RG;                 // rows per thread: 8 | 16
   constexpr int LPB = 32 / VEC;                // lanes per row block: 4 | 8
   constexpr int CB = FmtC<F>::bits;            // code bits
   constexpr bool ROWS = (AX & kRow) != 0;
   constexpr bool COLS = (AX & kCol) != 0;
+  constexpr int BPC = kTileR * CB / 8;         // staged code bytes per tile column: 128 | 64
+  constexpr int CPC = BPC / 16;                // 16-byte chunks per staged column: 8 | 4
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * kPitch : 16];
-  __shared__ uint8_t lds_scales[COLS ? kTileC * 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
+  __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * kWaveRows : 4];
 
-  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t per_batch = a.tiles_r * a.tiles_c;
-  const uint32_t bi = tile / per_batch;
-  const uint32_t rem = tile - bi * per_batch;
-  const uint32_t tr = rem / a.tiles_c;
-  const int64_t r0 = int64_t(tr) * kTileR;
-  const int64_t c0 = int64_t(rem - tr * a.tiles_c) * kTileC;
+  uint32_t bi, tr, tcol;
+  tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, bi, tr, tcol);
   const int64_t R = a.rows, C = a.cols;
+  const int64_t r0 = int64_t(tr) * kTileR;
+  const int64_t c0 = int64_t(tcol) * kTileC;
+  // rows / columns of this tile inside the tensor (ragged last tiles)
+  const int rows_in = int(min<int64_t>(R - r0, kTileR));
+  const int cols_in = int(min<int64_t>(C - c0, kTileC));
+  const uint32_t Cu = uint32_t(C);             // host guarantees C < 2^22 and, for columns, R < 2^23
 
-  const int wave = threadIdx.x >> 6;
+  const int wid = threadIdx.x >> 6;
+  const int wr = wid % kWaveRows, wc = wid / kWaveRows;
   const int lane = threadIdx.x & 63;
-  const int q = lane / LPR;
-  const int t = lane % LPR;
-  const int64_t col = c0 + int64_t(t) * VEC;
-  const int64_t row_base = r0 + 32 * wave + RPT * q;
-  const bool col_ok = col < C;
+  const int q = lane / LPR, t = lane % LPR;
+  const int lcol = 128 * wc + t * VEC;                    // column inside the tile
+  const int lrow = 32 * wr + RPT * q;                     // first row of this thread inside the tile
+  const bool col_ok = lcol < cols_in;
 
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + (int64_t(bi) * R * C) * (BF16 ? 2 : 4);
+  // tile origins (uniform across the workgroup) and 32-bit per-thread offsets
+  const int64_t tile_elem = (int64_t(bi) * R + r0) * C + c0;
+  const uint8_t* xt = reinterpret_cast<const uint8_t*>(a.x) + tile_elem * ES;
+  const uint32_t xoff = (uint32_t(lrow) * Cu + uint32_t(lcol)) * ES;
   uint4 v[RPT];
 #pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int64_t row = row_base + k;
-    if (col_ok && row < R)
-      v[k] = *reinterpret_cast<const uint4*>(xb + (row * C + col) * (BF16 ? 2 : 4));
-    else
-      v[k] = make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int k = 0; k < RPT; ++k)
+    v[k] = (col_ok && lrow + k < rows_in) ? load_nt(xt + xoff + uint32_t(k) * Cu * ES) : make_uint4(0u, 0u, 0u, 0u);
 
   // ---------------- row-wise blocks ----------------
   if constexpr (ROWS) {
-    uint8_t* rc = reinterpret_cast<uint8_t*>(a.row_codes);
+    uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem * CB / 8;
+    const uint32_t rcoff = (uint32_t(lrow) * Cu + uint32_t(lcol)) * CB / 8;
+    uint32_t scale_dw = 0;                      // 4 scale bytes of one row's 128 wave columns, lane t == k
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      const int64_t row = row_base + k;
       uint32_t m;
       if constexpr (BF16) {
-        uint32_t h = pk_max_u16(pk_max_u16(v[k].x & 0x7FFF7FFFu, v[k].y & 0x7FFF7FFFu),
-                                pk_max_u16(v[k].z & 0x7FFF7FFFu, v[k].w & 0x7FFF7FFFu));
+        const uint32_t h = pk_max_u16(pk_max_u16(v[k].x & 0x7FFF7FFFu, v[k].y & 0x7FFF7FFFu),
+                                      pk_max_u16(v[k].z & 0x7FFF7FFFu, v[k].w & 0x7FFF7FFFu));
         m = max(h & 0xFFFFu, h >> 16);
       } else {
-        m = max(max(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu),
-                max(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu));
+        m = max(max(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu), max(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu));
       }
-#pragma unroll
-      for (int s = 1; s < LPB; s <<= 1) m = xor_max(m, s);
+      m = group_max<LPB>(m);
       const uint32_t code = scale_code<F, M, BF16>(m);
-      const bool ok = col_ok && row < R;
-      const int64_t e0 = (int64_t(bi) * R + row) * C + col;   // element index
+      const bool ok = col_ok && lrow + k < rows_in;
+      uint8_t* dst = rct + rcoff + uint32_t(k) * Cu * CB / 8;
       if constexpr (BF16) {
         const uint2 w = encode8_bf16<F, M>(v[k].x, v[k].y, v[k].z, v[k].w, code);
         if (ok) {
-          if constexpr (CB == 8) *reinterpret_cast<uint2*>(rc + e0) = w;
-          else *reinterpret_cast<uint32_t*>(rc + e0 / 2) = w.x;
+          if constexpr (CB == 8) store_nt8(dst, w);
+          else store_nt4(dst, w.x);
         }
       } else {
         const uint32_t w = encode4_f32<F, M>(__uint_as_float(v[k].x), __uint_as_float(v[k].y),
                                              __uint_as_float(v[k].z), __uint_as_float(v[k].w), code);
         if (ok) {
-          if constexpr (CB == 8) *reinterpret_cast<uint32_t*>(rc + e0) = w;
-          else *reinterpret_cast<uint16_t*>(rc + e0 / 2) = uint16_t(w);
+          if constexpr (CB == 8) store_nt4(dst, w);
+          else store_nt2(dst, w);
         }
       }
-      if (ok && (t % LPB) == 0) a.row_scales[e0 / 32] = uint8_t(code);
+      // OR the 4 block codes of this wave row into one dword: lanes t, t^LPB, ..
+      uint32_t sb = code << (8 * (t / LPB));
+      if constexpr (BF16) {
+        sb |= dpp<kDppRor4>(sb);
+        sb |= dpp<kDppRor8>(sb);
+      } else {
+        sb |= dpp<kDppRor8>(sb);
+        sb = or_xor16(sb);
+      }
+      scale_dw = (t == k) ? sb : scale_dw;
+    }
+    // lane t < RPT stores the scale bytes of tile row lrow + t, wave columns 128*wc .. +127
+    if (t < RPT && lrow + t < rows_in && 128 * wc < cols_in) {
+      uint8_t* dst = a.row_scales + tile_elem / 32 + (uint32_t(lrow + t) * Cu + uint32_t(128 * wc)) / 32;
+      if (a.flags & kRowScaleDword) {
+        *reinterpret_cast<uint32_t*>(dst) = scale_dw;
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (128 * wc + 32 * m < cols_in) dst[m] = uint8_t(scale_dw >> (8 * m));
+      }
     }
   }
 
   // ---------------- column-wise blocks ----------------
   if constexpr (COLS) {
-    constexpr int CPL = CB == 8 ? RPT : RPT / 2;      // code bytes per column per thread
-    const int row_in_tile = 32 * wave + RPT * q;        // first tile row of this thread
     uint32_t code_j[VEC];
     if constexpr (BF16) {
       uint32_t cm[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t* p0 = &v[0].x;
-        cm[d] = p0[d] & 0x7FFF7FFFu;
-      }
+      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFF7FFFu;
 #pragma unroll
       for (int k = 1; k < RPT; ++k) {
-        const uint32_t* pk = &v[k].x;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], pk[d] & 0x7FFF7FFFu);
+        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], (&v[k].x)[d] & 0x7FFF7FFFu);
       }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int s = LPR; s < 64; s <<= 1) cm[d] = xor_max_pk16(cm[d], s);
+        cm[d] = pk_max_xor32(pk_max_xor16(cm[d]));     // the 4 row groups of the 32-row block
         code_j[2 * d] = scale_code<F, M, true>(cm[d] & 0xFFFFu);
         code_j[2 * d + 1] = scale_code<F, M, true>(cm[d] >> 16);
-      }
-      // encode: column j = 2d + h; rows k, k+1 paired via byte permute
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const int d = j >> 1;
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t pr[RPT / 2];
-#pragma unroll
-        for (int k = 0; k < RPT; k += 2) {
-          const uint32_t* pa = &v[k].x;
-          const uint32_t* pb = &v[k + 1].x;
-          pr[k / 2] = __builtin_amdgcn_perm(pb[d], pa[d], sel);
-        }
-        const uint2 w = encode8_bf16<F, M>(pr[0], pr[1], pr[2], pr[3], code_j[j]);
-        uint8_t* dst = lds_codes + (t * VEC + j) * kPitch + row_in_tile * CB / 8;
-        if constexpr (CB == 8) *reinterpret_cast<uint2*>(dst) = w;
-        else *reinterpret_cast<uint32_t*>(dst) = w.x;
       }
     } else {
       uint32_t cm[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t* p0 = &v[0].x;
-        cm[d] = p0[d] & 0x7FFFFFFFu;
-      }
+      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFFFFFFu;
 #pragma unroll
       for (int k = 1; k < RPT; ++k) {
-        const uint32_t* pk = &v[k].x;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) cm[d] = max(cm[d], pk[d] & 0x7FFFFFFFu);
+        for (int d = 0; d < 4; ++d) cm[d] = max(cm[d], (&v[k].x)[d] & 0x7FFFFFFFu);
       }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int s = LPR; s < 64; s <<= 1) cm[d] = xor_max(cm[d], s);
+        cm[d] = max_xor32(cm[d]);                      // the 2 row groups of the 32-row block
         code_j[d] = scale_code<F, M, false>(cm[d]);
       }
+    }
+    // encode column j of this thread (rows lrow .. +RPT-1) and stage it at
+    // [column][row], the 16-byte chunk index XORed with (column / 8) mod CPC
+    const int byte0 = lrow * CB / 8;                  // this thread's offset inside a staged column
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
+    for (int j = 0; j < VEC; ++j) {
+      const int cl = lcol + j;
+      const int off = cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
+      if constexpr (BF16) {
+        const int d = j >> 1;
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t pr[4];
+#pragma unroll
+        for (int k = 0; k < RPT; k += 2) pr[k / 2] = __builtin_amdgcn_perm((&v[k + 1].x)[d], (&v[k].x)[d], sel);
+        const uint2 w = encode8_bf16<F, M>(pr[0], pr[1], pr[2], pr[3], code_j[j]);
+        if constexpr (CB == 8) *reinterpret_cast<uint2*>(lds_codes + off) = w;       // 8 rows
+        else *reinterpret_cast<uint32_t*>(lds_codes + off) = w.x;                   // 8 rows in 4 bytes
+      } else {
         uint32_t w[RPT / 4];
 #pragma unroll
-        for (int g = 0; g < RPT / 4; ++g) {
-          const uint32_t* r0p = &v[4 * g].x;
-          const uint32_t* r1p = &v[4 * g + 1].x;
-          const uint32_t* r2p = &v[4 * g + 2].x;
-          const uint32_t* r3p = &v[4 * g + 3].x;
-          w[g] = encode4_f32<F, M>(__uint_as_float(r0p[j]), __uint_as_float(r1p[j]),
-                                   __uint_as_float(r2p[j]), __uint_as_float(r3p[j]), code_j[j]);
-        }
-        uint8_t* dst = lds_codes + (t * VEC + j) * kPitch + row_in_tile * CB / 8;
+        for (int g = 0; g < RPT / 4; ++g)
+          w[g] = encode4_f32<F, M>(__uint_as_float((&v[4 * g].x)[j]), __uint_as_float((&v[4 * g + 1].x)[j]),
+                                   __uint_as_float((&v[4 * g + 2].x)[j]), __uint_as_float((&v[4 * g + 3].x)[j]),
+                                   code_j[j]);
         if constexpr (CB == 8) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+          *reinterpret_cast<uint4*>(lds_codes + off) = make_uint4(w[0], w[1], w[2], w[3]);   // 16 rows
         } else {
-          *reinterpret_cast<uint2*>(dst) =
+          *reinterpret_cast<uint2*>(lds_codes + off) =
               make_uint2((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16));
         }
       }
     }
     if (q == 0) {
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) lds_scales[(t * VEC + j) * 4 + wave] = uint8_t(code_j[j]);
+      for (int j = 0; j < VEC; ++j) lds_scales[(lcol + j) * kWaveRows + wr] = uint8_t(code_j[j]);
     }
     __syncthreads();
 
-    // transposed write-out: column c of the tile -> row (c0 + c) of the column plane
-    constexpr int BPC = kTileR * CB / 8;               // code bytes per staged column
-    constexpr int CPC = BPC / 16;                      // 16-byte chunks per column
+    // transposed write-out: tile column cl -> row (c0 + cl) of the column plane
     constexpr int ROWS_PER_CHUNK = 16 * 8 / CB;
-    uint8_t* cc = reinterpret_cast<uint8_t*>(a.col_codes);
+    const uint32_t Ru = uint32_t(R);
+    const int64_t ctile_elem = (int64_t(bi) * C + c0) * R + r0;
+    uint8_t* cct = reinterpret_cast<uint8_t*>(a.col_codes) + ctile_elem * CB / 8;
 #pragma unroll
     for (int i = 0; i < kTileC * CPC / kThreads; ++i) {
       const int id = threadIdx.x + i * kThreads;
       const int cl = id / CPC;
       const int part = id % CPC;
-      const int64_t oc = c0 + cl;
-      const int64_t orow = r0 + int64_t(part) * ROWS_PER_CHUNK;
-      if (oc < C && orow < R) {
-        const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * kPitch + part * 16);
-        const int64_t e0 = (int64_t(bi) * C + oc) * R + orow;
-        *reinterpret_cast<uint4*>(cc + e0 * CB / 8) = w;
+      if (cl < cols_in && part * ROWS_PER_CHUNK < rows_in) {
+        const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+        *reinterpret_cast<uint4*>(cct + uint32_t(cl) * Ru * CB / 8 + uint32_t(part) * 16) = w;
       }
     }
-    if (threadIdx.x < kTileC) {
+    if (int(threadIdx.x) < cols_in) {
       const int cl = threadIdx.x;
-      const int64_t oc = c0 + cl;
-      if (oc < C) {
-        uint8_t* dst = a.col_scales + ((int64_t(bi) * C + oc) * R + r0) / 32;
+      uint8_t* dst = a.col_scales + ctile_elem / 32 + uint32_t(cl) * Ru / 32;
+      if (a.flags & kColScaleDword) {
+        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scales + cl * kWaveRows);
+      } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          if (r0 + 32 * w < R) dst[w] = lds_scales[cl * 4 + w];
+        for (int w = 0; w < kWaveRows; ++w)
+          if (32 * w < rows_in) dst[w] = lds_scales[cl * kWaveRows + w];
       }
     }
   }

@@ -166,18 +166,52 @@ __device__ __forceinline__ uint32_t encode4_f32(float f0, float f1, float f2, fl
   return code == 0xFFu ? FmtC<F>::nan_fill : w;
 }
 
-// max over 16-bit halves, then the two halves folded together.
+// max over the two 16-bit halves independently (v_pk_max_u16).
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
-  uint32_t hi = max(a >> 16, b >> 16);
-  return lo | (hi << 16);
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
 }
 
-__device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
-  return max(v, (uint32_t)__shfl_xor((int)v, mask, 64));
+// Cross-lane moves without LDS. DPP patterns act inside each 16-lane row:
+// quad_perm [1,0,3,2] = lane ^ 1, [2,3,0,1] = lane ^ 2, row_half_mirror maps
+// lane i of an 8-lane half to 7 - i, row_ror:n rotates the row by n lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t xor_max_pk16(uint32_t v, int mask) {
-  return pk_max_u16(v, (uint32_t)__shfl_xor((int)v, mask, 64));
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+// gfx950 v_permlane{16,32}_swap with both operands equal: the two results
+// hold, for every lane, its own value and the value of lane ^ 16 (resp. ^ 32).
+__device__ __forceinline__ uint32_t max_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ uint32_t pk_max_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return pk_max_u16(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ uint32_t pk_max_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return pk_max_u16(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ uint32_t or_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return uint32_t(r[0]) | uint32_t(r[1]);
+}
+
+// Max over aligned groups of N lanes (N = 4 or 8) inside a 16-lane row.
+template <int N>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  if constexpr (N == 8) v = max(v, dpp<kDppHalfMirror>(v));
+  return v;
 }
 
 }  // namespace mx

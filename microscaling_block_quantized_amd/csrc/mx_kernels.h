@@ -16,7 +16,13 @@ struct CastArgs {
   uint8_t* col_scales;    // [batch][cols][rows/32] or null
   int64_t rows, cols;     // per batch slice
   uint32_t tiles_r, tiles_c;
+  uint32_t flags;         // kRowScaleDword / kColScaleDword
 };
+
+// A tile's 4 scale bytes per row (column) may be stored as one dword: the
+// plane's row pitch is a multiple of 4 bytes and its base is 4-byte aligned.
+constexpr uint32_t kRowScaleDword = 1u;
+constexpr uint32_t kColScaleDword = 2u;
 
 struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;
