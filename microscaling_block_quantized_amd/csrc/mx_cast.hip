@@ -78,7 +78,7 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nb, uint32_t 
 }
 
 template <bool BF16, int F, int M, int AX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 3))) void mx_cast_kernel(CastArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : (AX == kBoth ? 2 : 3)))) void mx_cast_kernel(CastArgs a) {
   constexpr int VEC = InC<BF16>::vec;          // elements per 16-byte chunk
   constexpr int ES = BF16 ? 2 : 4;             // input element bytes
   constexpr int LPR = 128 / VEC;               // lanes per 128-column wave row: 16 | 32
@@ -116,10 +116,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   const int64_t tile_elem = (int64_t(bi) * R + r0) * C + c0;
   const uint8_t* xt = reinterpret_cast<const uint8_t*>(a.x) + tile_elem * ES;
   const uint32_t xoff = (uint32_t(lrow) * Cu + uint32_t(lcol)) * ES;
+  // Every lane loads (lanes outside a ragged tile read the tile origin, which
+  // always exists, and then zero their data), so the 8 or 16 loads issue back
+  // to back without branches between them.
   uint4 v[RPT];
 #pragma unroll
-  for (int k = 0; k < RPT; ++k)
-    v[k] = (col_ok && lrow + k < rows_in) ? load_nt(xt + xoff + uint32_t(k) * Cu * ES) : make_uint4(0u, 0u, 0u, 0u);
+  for (int k = 0; k < RPT; ++k) {
+    const bool ok = col_ok && lrow + k < rows_in;
+    const uint4 d = load_nt(xt + (ok ? xoff + uint32_t(k) * Cu * ES : 0u));
+    v[k] = ok ? d : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Column-block maxima need every row this thread loaded, so they are formed
+  // first: the loads are all consumed before the first store is issued, and no
+  // wait on the vector-memory counter (which also counts stores) sits between
+  // the stores below.
+  uint32_t code_j[COLS ? VEC : 1];
+  if constexpr (COLS) {
+    uint32_t cm[4];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFF7FFFu;
+#pragma unroll
+      for (int k = 1; k < RPT; ++k) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], (&v[k].x)[d] & 0x7FFF7FFFu);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        cm[d] = pk_max_xor32(pk_max_xor16(cm[d]));       // the 4 row groups of the 32-row block
+        code_j[2 * d] = scale_code<F, M, true>(cm[d] & 0xFFFFu);
+        code_j[2 * d + 1] = scale_code<F, M, true>(cm[d] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFFFFFFu;
+#pragma unroll
+      for (int k = 1; k < RPT; ++k) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) cm[d] = max(cm[d], (&v[k].x)[d] & 0x7FFFFFFFu);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        cm[d] = max_xor32(cm[d]);                        // the 2 row groups of the 32-row block
+        code_j[d] = scale_code<F, M, false>(cm[d]);
+      }
+    }
+  }
 
   // ---------------- row-wise blocks ----------------
   if constexpr (ROWS) {
@@ -180,37 +223,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 
   // ---------------- column-wise blocks ----------------
   if constexpr (COLS) {
-    uint32_t code_j[VEC];
-    if constexpr (BF16) {
-      uint32_t cm[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFF7FFFu;
-#pragma unroll
-      for (int k = 1; k < RPT; ++k) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], (&v[k].x)[d] & 0x7FFF7FFFu);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        cm[d] = pk_max_xor32(pk_max_xor16(cm[d]));     // the 4 row groups of the 32-row block
-        code_j[2 * d] = scale_code<F, M, true>(cm[d] & 0xFFFFu);
-        code_j[2 * d + 1] = scale_code<F, M, true>(cm[d] >> 16);
-      }
-    } else {
-      uint32_t cm[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) cm[d] = (&v[0].x)[d] & 0x7FFFFFFFu;
-#pragma unroll
-      for (int k = 1; k < RPT; ++k) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) cm[d] = max(cm[d], (&v[k].x)[d] & 0x7FFFFFFFu);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        cm[d] = max_xor32(cm[d]);                      // the 2 row groups of the 32-row block
-        code_j[d] = scale_code<F, M, false>(cm[d]);
-      }
-    }
     // encode column j of this thread (rows lrow .. +RPT-1) and stage it at
     // [column][row], the 16-byte chunk index XORed with (column / 8) mod CPC
     const int byte0 = lrow * CB / 8;                  // this thread's offset inside a staged column
