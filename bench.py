@@ -150,13 +150,127 @@ def cpu_baseline(x_gpu, budget_s: float = 12.0):
                       f"E4M3 floor, NumPy float64 oracle, single thread, {t_used:.1f} s"}
 
 
+def _planes(dev, b, r, c, fmt, axis):
+    import torch
+    div = 2 if fmt == "e2m1" else 1
+    out = {}
+    if axis in ("row", "both"):
+        out["row_codes"] = torch.empty((b, r, c // div), dtype=torch.uint8, device=dev)
+        out["row_scales"] = torch.empty((b, r, c // 32), dtype=torch.uint8, device=dev)
+    if axis in ("col", "both"):
+        out["col_codes"] = torch.empty((b, c, r // div), dtype=torch.uint8, device=dev)
+        out["col_scales"] = torch.empty((b, c, r // 32), dtype=torch.uint8, device=dev)
+    return out
+
+
+def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc):
+    """One quantize launch per step over one tensor; bytes = input + code and scale planes."""
+    planes = (2 if axis == "both" else 1)
+    nbytes = b * r * c * esize + planes * (b * r * c * (4 if fmt == "e2m1" else 8) // 8 + b * r * c // 32)
+
+    def make(dev, i):
+        import microscaling_block_quantized_amd as mx
+        x = gen(dev, i).reshape(b, r, c)
+        return mx.BoundQuantize(x, fmt, mode, axis, _planes(dev, b, r, c, fmt, axis))
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+            "config": {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": fmt, "scale_mode": mode,
+                       "axis": axis}}
+
+
+def _wide_range_pipeline():
+    """64 x 4096x14336 BF16: fused E4M3 quantize, then both planes dequantized to BF16."""
+    b, r, c = 64, 4096, 14336
+    n = b * r * c
+    nbytes = (n * 2 + 2 * (n + n // 32)) + 2 * (n + n // 32 + n * 2)
+
+    def make(dev, i):
+        import torch
+        import microscaling_block_quantized_amd as mx
+        import mx_inputs as I
+        x = I.wide_range_batch(b, r, c, seed=4 + 100 * i, device=dev)
+        planes = _planes(dev, b, r, c, "e4m3", "both")
+        q = mx.BoundQuantize(x, "e4m3", "floor", "both", planes)
+        yr = torch.empty((b, r, c), dtype=torch.bfloat16, device=dev)
+        yc = torch.empty((b, c, r), dtype=torch.bfloat16, device=dev)
+        dr = mx.BoundDequantize(planes["row_codes"], planes["row_scales"], "e4m3", (b, r, c), yr)
+        dc = mx.BoundDequantize(planes["col_codes"], planes["col_scales"], "e4m3", (b, c, r), yc)
+
+        def step():
+            q()
+            dr()
+            dc()
+        return step
+    return {"bytes": nbytes, "make": make,
+            "metric": "GB/s (read+write), 64x4096x14336 BF16 MXFP8 E4M3 row+col quantize + both dequantizes",
+            "config": {"workload": "wide-range batch 64x4096x14336 bf16: fused E4M3 quantize (floor), then "
+                                   "row and column planes dequantized to bf16",
+                       "batch": b, "rows": r, "cols": c, "fmt": "e4m3", "scale_mode": "floor", "axis": "both"}}
+
+
+def _fp32_normal_round_trip():
+    """256x1024 FP32 N(0,1): row-wise E4M3 quantize (floor) + dequantize to FP32."""
+    r, c = 256, 1024
+    n = r * c
+    nbytes = (n * 4 + n + n // 32) + (n + n // 32 + n * 4)
+
+    def make(dev, i):
+        import torch
+        import microscaling_block_quantized_amd as mx
+        import mx_inputs as I
+        x = I.fp32_normal(r, c, seed=i, device=dev)
+        planes = _planes(dev, 1, r, c, "e4m3", "row")
+        q = mx.BoundQuantize(x.view(1, r, c), "e4m3", "floor", "row", planes)
+        y = torch.empty((1, r, c), dtype=torch.float32, device=dev)
+        d = mx.BoundDequantize(planes["row_codes"], planes["row_scales"], "e4m3", (1, r, c), y)
+
+        def step():
+            q()
+            d()
+        return step
+    return {"bytes": nbytes, "make": make,
+            "metric": "GB/s (read+write), 256x1024 FP32 MXFP8 E4M3 row quantize + dequantize",
+            "config": {"workload": "fp32 N(0,1) 256x1024: row-wise E4M3 quantize (floor) + dequantize to fp32",
+                       "rows": r, "cols": c, "fmt": "e4m3", "scale_mode": "floor", "axis": "row"}}
+
+
+def _gen(name):
+    def g(dev, i):
+        import mx_inputs as I
+        if name == "activations":
+            return I.activations(ROWS, COLS, seed=1 + i, device=dev)
+        if name == "weights":
+            return I.weights(14336, 4096, seed=2 + 100 * i, device=dev)
+        if name == "gradients":
+            return I.gradients(8192, 8192, seed=3 + 100 * i, device=dev)
+        raise KeyError(name)
+    return g
+
+
+WORKLOADS = {
+    "activations": _cast_workload(_gen("activations"), 1, ROWS, COLS, 2, "e4m3", "floor", "both",
+                                  "activations 16384x4096 bf16 -> MXFP8 E4M3 row+col fused, floor scale rule"),
+    "weights_floor": _cast_workload(_gen("weights"), 1, 14336, 4096, 2, "e2m1", "floor", "row",
+                                    "weights 14336x4096 bf16 -> MXFP4 E2M1 row-wise, floor scale rule"),
+    "weights_roundup": _cast_workload(_gen("weights"), 1, 14336, 4096, 2, "e2m1", "roundup", "row",
+                                      "weights 14336x4096 bf16 -> MXFP4 E2M1 row-wise, round-up scale rule"),
+    "gradients": _cast_workload(_gen("gradients"), 1, 8192, 8192, 4, "e5m2", "roundup", "col",
+                                "gradients 8192x8192 fp32 -> MXFP8 E5M2 column-wise, round-up scale rule"),
+    "wide_range": _wide_range_pipeline(),
+    "fp32_normal": _fp32_normal_round_trip(),
+}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=3, help="rotating input/output buffer sets")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating input/output buffer sets (default 3; 1 for the 30 GB wide-range batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="activations", choices=sorted(WORKLOADS),
+                    help="activations (default) is the fused row+col MXFP8 cast the metric is quoted on; "
+                         "the others time the remaining workloads the same way")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -177,25 +291,17 @@ def main() -> int:
     import torch
 
     import microscaling_block_quantized_amd as mx
-    import mx_inputs as I
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    xs, calls = [], []
-    for i in range(args.sets):
-        x = I.activations(ROWS, COLS, seed=1 + i, device=dev)
-        out = {
-            "row_codes": torch.empty((1, ROWS, COLS), dtype=torch.uint8, device=dev),
-            "row_scales": torch.empty((1, ROWS, COLS // 32), dtype=torch.uint8, device=dev),
-            "col_codes": torch.empty((1, COLS, ROWS), dtype=torch.uint8, device=dev),
-            "col_scales": torch.empty((1, COLS, ROWS // 32), dtype=torch.uint8, device=dev),
-        }
-        xs.append(x)
-        calls.append(mx.BoundQuantize(x, "e4m3", "floor", "both", out))
+    wl = WORKLOADS[args.workload]
+    if args.sets <= 0:
+        args.sets = 1 if args.workload == "wide_range" else 3
+    steps_fns = [wl["make"](dev, i) for i in range(args.sets)]
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        calls[i % args.sets]()
+        steps_fns[i % args.sets]()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -204,13 +310,18 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        calls[i % args.sets]()
+        steps_fns[i % args.sets]()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    alg_bytes = wl["bytes"]
+    del steps_fns
+    torch.cuda.empty_cache()
 
-    # a plain device copy of the same read+write byte count, as a measured ceiling
-    src = torch.empty(ALG_BYTES // 2, dtype=torch.uint8, device=dev)
+    # a plain device copy as a measured ceiling: the workload's read+write byte
+    # count, but at least 256 MiB each way so four buffers exceed the 256 MB cache
+    copy_half = min(max(alg_bytes // 2, 1 << 28), 1 << 31)
+    src = torch.empty(copy_half, dtype=torch.uint8, device=dev)
     dsts = [torch.empty_like(src) for _ in range(3)]
     for d in dsts:
         d.copy_(src)
@@ -222,13 +333,13 @@ def main() -> int:
         dsts[i % 3].copy_(src)
     c1.record(stream)
     torch.cuda.synchronize()
-    copy_gbs = ALG_BYTES / (c0.elapsed_time(c1) / 30 * 1e-3) / 1e9
+    copy_gbs = 2 * copy_half / (c0.elapsed_time(c1) / 30 * 1e-3) / 1e9
     del src, dsts
 
-    gbs = ALG_BYTES / (ms * 1e-3) / 1e9
-    traffic = read_counters()
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = read_counters() if args.workload == "activations" else None
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "activations" else wl["metric"],
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -240,18 +351,17 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "activations 16384x4096 bf16 -> MXFP8 E4M3 row+col fused, floor scale rule",
-                   "rows": ROWS, "cols": COLS, "fmt": "e4m3", "scale_mode": "floor", "axis": "both",
-                   "buffer_sets": args.sets},
+        "config": dict(wl["config"], buffer_sets=args.sets, alg_bytes_per_step=alg_bytes),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "copy_ceiling": {"value": round(copy_gbs, 2), "unit": "GB/s",
-                         "what": "torch device copy moving the same read+write bytes",
+                         "what": f"torch device copy, {copy_half} B each way, 3 rotating destinations",
                          "frac_of_ceiling": round(gbs / copy_gbs, 4)},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(xs[0])
+    if not args.no_cpu_baseline and args.workload == "activations":
+        import mx_inputs as I
+        line["cpu_baseline"] = cpu_baseline(I.activations(ROWS, COLS, seed=1, device=dev))
     print(json.dumps(line))
     return 0
 

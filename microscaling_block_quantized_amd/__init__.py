@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "MXError", "FMT", "MODE", "AXIS", "DTYPE", "lib_path", "load", "mx_version", "mx_strerror",
-    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize",
+    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize", "BoundDequantize",
 ]
 
 FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
@@ -191,3 +191,20 @@ class BoundQuantize:
         err = self._fn(*self._args)
         if err:
             raise MXError(err, "mx_quantize")
+
+
+class BoundDequantize:
+    """An mx_dequantize call with its arguments marshalled once (see BoundQuantize)."""
+
+    def __init__(self, codes, scales, fmt: str, shape, y):
+        import torch
+        b, r, c = _shape3(shape)
+        self._fn = load().mx_dequantize
+        self._args = (_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c),
+                      DTYPE["bf16" if y.dtype == torch.bfloat16 else "f32"], _ptr(y), _stream_of(codes))
+        self._keep = (codes, scales, y)
+
+    def __call__(self) -> None:
+        err = self._fn(*self._args)
+        if err:
+            raise MXError(err, "mx_dequantize")
