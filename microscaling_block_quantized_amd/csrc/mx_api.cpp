@@ -103,7 +103,7 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
     for (int j = i + 1; j < nr; ++j)
       if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
 
-  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols);
+  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, int(axis));
   if (g.blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
   // per-thread offsets inside a tile are 32-bit: 128 rows of FP32 and 256 column-plane rows
   if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;
@@ -116,10 +116,14 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
   a.col_scales = col_scales;
   a.rows = s.rows;
   a.cols = s.cols;
+  a.elements = n;
   a.tiles_r = uint32_t(g.tiles_r);
   a.tiles_c = uint32_t(g.tiles_c);
   a.flags = 0;
-  if (want_row && s.cols % 128 == 0 && aligned(row_scales, 4)) a.flags |= mx::kRowScaleDword;
+  // the row-only kernel stores 4 scale bytes of consecutive blocks at once (any cols);
+  // the tiled kernel stores the 4 of one row's 128 columns (cols % 128 == 0)
+  if (want_row && aligned(row_scales, 4) && (axis == MX_AXIS_ROW || s.cols % 128 == 0))
+    a.flags |= mx::kRowScaleDword;
   if (want_col && s.rows % 128 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
   const hipError_t e = mx::launch_cast(x_dtype == MX_BF16, int(fmt), int(mode), int(axis), a,
                                        uint32_t(g.blocks), static_cast<hipStream_t>(stream));

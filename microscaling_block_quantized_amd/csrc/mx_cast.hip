@@ -289,6 +289,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   }
 }
 
+// Row-wise only: the blocks are 32 consecutive elements of the flat
+// [batch][rows][cols] order, so the cast is a linear stream. Lane i of a wave
+// handles 16-byte chunk i of each 1 KiB wave step (4 (BF16) or 8 (FP32) lanes
+// per block); kRowSteps steps per wave are in flight at once. The 4 scale
+// bytes of 4 neighbouring blocks are ORed into one dword store.
+constexpr int kRowThreads = 256;
+constexpr int kRowSteps = 2;
+
+template <bool BF16, int F, int M>
+__global__ __launch_bounds__(kRowThreads) void mx_cast_rows_kernel(CastArgs a, int64_t nchunks) {
+  constexpr int VEC = InC<BF16>::vec;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int LPB = 32 / VEC;                 // lanes per block: 4 | 8
+  constexpr int LPG = 4 * LPB;                  // lanes per 4-block scale group: 16 | 32
+  constexpr int CB = FmtC<F>::bits;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_global = int64_t(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
+  const int64_t chunk0 = wave_global * (64 * kRowSteps) + lane;
+  const uint8_t* x = reinterpret_cast<const uint8_t*>(a.x);
+  uint8_t* rc = reinterpret_cast<uint8_t*>(a.row_codes);
+
+  uint4 v[kRowSteps];
+#pragma unroll
+  for (int u = 0; u < kRowSteps; ++u) {
+    const int64_t ch = chunk0 + 64 * u;
+    const bool ok = ch < nchunks;
+    const uint4 d = load_nt(x + (ok ? ch : 0) * 16);
+    v[u] = ok ? d : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < kRowSteps; ++u) {
+    const int64_t ch = chunk0 + 64 * u;
+    uint32_t m;
+    if constexpr (BF16) {
+      const uint32_t h = pk_max_u16(pk_max_u16(v[u].x & 0x7FFF7FFFu, v[u].y & 0x7FFF7FFFu),
+                                    pk_max_u16(v[u].z & 0x7FFF7FFFu, v[u].w & 0x7FFF7FFFu));
+      m = max(h & 0xFFFFu, h >> 16);
+    } else {
+      m = max(max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu), max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu));
+    }
+    m = group_max<LPB>(m);
+    const uint32_t code = scale_code<F, M, BF16>(m);
+    const int64_t e0 = ch * VEC;                       // first element of this chunk
+    if constexpr (BF16) {
+      const uint2 w = encode8_bf16<F, M>(v[u].x, v[u].y, v[u].z, v[u].w, code);
+      if (ch < nchunks) {
+        if constexpr (CB == 8) store_nt8(rc + e0, w);
+        else store_nt4(rc + e0 / 2, w.x);
+      }
+    } else {
+      const uint32_t w = encode4_f32<F, M>(__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                                           __uint_as_float(v[u].z), __uint_as_float(v[u].w), code);
+      if (ch < nchunks) {
+        if constexpr (CB == 8) store_nt4(rc + e0, w);
+        else store_nt2(rc + e0 / 2, w);
+      }
+    }
+    // scale bytes of the 4 blocks of this lane's group, lane 0 of the group stores
+    uint32_t sb = code << (8 * ((lane % LPG) / LPB));
+    if constexpr (BF16) {
+      sb |= dpp<kDppRor4>(sb);
+      sb |= dpp<kDppRor8>(sb);
+    } else {
+      sb |= dpp<kDppRor8>(sb);
+      sb = or_xor16(sb);
+    }
+    if ((lane % LPG) == 0 && ch < nchunks) {
+      const int64_t blk = e0 / 32;                     // multiple of 4
+      const int64_t nblk = nchunks / LPB;
+      if ((a.flags & kRowScaleDword) && blk + 4 <= nblk) {
+        *reinterpret_cast<uint32_t*>(a.row_scales + blk) = sb;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (blk + b < nblk) a.row_scales[blk + b] = uint8_t(sb >> (8 * b));
+      }
+    }
+  }
+}
+
+template <bool BF16, int F, int M>
+hipError_t launch_rows(const CastArgs& a, int64_t nchunks, hipStream_t s) {
+  const int64_t per_block = int64_t(kRowThreads / 64) * 64 * kRowSteps;
+  const int64_t blocks = (nchunks + per_block - 1) / per_block;
+  hipLaunchKernelGGL((mx_cast_rows_kernel<BF16, F, M>), dim3(uint32_t(blocks)), dim3(kRowThreads), 0, s, a, nchunks);
+  return hipGetLastError();
+}
+
 template <bool BF16, int F, int M, int AX>
 hipError_t launch_one(const CastArgs& a, uint32_t nblocks, hipStream_t s) {
   hipLaunchKernelGGL((mx_cast_kernel<BF16, F, M, AX>), dim3(nblocks), dim3(kThreads), 0, s, a);
@@ -298,7 +386,7 @@ hipError_t launch_one(const CastArgs& a, uint32_t nblocks, hipStream_t s) {
 template <bool BF16, int F, int M>
 hipError_t by_axis(int axis, const CastArgs& a, uint32_t nb, hipStream_t s) {
   switch (axis) {
-    case kRow: return launch_one<BF16, F, M, kRow>(a, nb, s);
+    case kRow: return launch_rows<BF16, F, M>(a, a.elements / InC<BF16>::vec, s);
     case kCol: return launch_one<BF16, F, M, kCol>(a, nb, s);
     default: return launch_one<BF16, F, M, kBoth>(a, nb, s);
   }
@@ -321,11 +409,16 @@ hipError_t by_fmt(int fmt, int mode, int axis, const CastArgs& a, uint32_t nb, h
 
 }  // namespace
 
-CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols) {
+CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, int axis) {
   CastGrid g;
   g.tiles_r = (rows + kTileR - 1) / kTileR;
   g.tiles_c = (cols + kTileC - 1) / kTileC;
-  g.blocks = batch * g.tiles_r * g.tiles_c;
+  if (axis == kRow) {
+    const int64_t per_block = int64_t(kRowThreads / 64) * 64 * kRowSteps * 8;   // elements (BF16 bound)
+    g.blocks = (batch * rows * cols + per_block - 1) / per_block * 2;           // FP32 needs twice as many
+  } else {
+    g.blocks = batch * g.tiles_r * g.tiles_c;
+  }
   return g;
 }
 

@@ -15,6 +15,7 @@ struct CastArgs {
   void* col_codes;        // [batch][cols][rows] (E2M1: [..][rows/2]) or null
   uint8_t* col_scales;    // [batch][cols][rows/32] or null
   int64_t rows, cols;     // per batch slice
+  int64_t elements;       // batch * rows * cols
   uint32_t tiles_r, tiles_c;
   uint32_t flags;         // kRowScaleDword / kColScaleDword
 };
@@ -28,7 +29,8 @@ struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;
 };
 
-CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols);
+// Launch geometry; `blocks` bounds the workgroup count of the chosen kernel.
+CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, int axis);
 hipError_t launch_cast(bool in_bf16, int fmt, int mode, int axis, const CastArgs& a,
                        uint32_t nblocks, hipStream_t s);
 
