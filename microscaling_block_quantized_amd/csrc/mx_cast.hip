@@ -21,12 +21,13 @@
 //     the RG lanes holding the other rows of the block. The codes (1 byte, not
 //     the inputs) are staged in LDS as [column][row] with a 16-byte XOR swizzle
 //     and written out as 128-byte runs of the transposed plane.
-// Memory-system choices, all measured on MI355X for the 16384x4096 fused
-// cast: the input is read and the row codes are written with non-temporal
-// accesses, while the transposed column runs and the scale planes go through
-// L2 with ordinary stores (scale bytes of one 128-byte line come from several
-// workgroups and must merge in L2). Tiles are ordered so that each XCD owns a
-// strip of adjacent tile columns and sweeps down the rows.
+// Memory-system choices, measured on MI355X with input and output buffers
+// rotated through more memory than the 256 MB last-level cache holds: the
+// input is read and both code planes are written with non-temporal accesses,
+// while the scale planes go through L2 with ordinary stores (scale bytes of one
+// 128-byte line come from several workgroups and must merge in L2; making them
+// non-temporal costs 60%). Tiles are ordered so that each XCD owns a strip of
+// adjacent tile columns and sweeps down the rows.
 #include "mx_kernels.h"
 
 namespace mx {
@@ -46,6 +47,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
 __device__ __forceinline__ void store_nt8(void* p, uint2 v) {
   __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int part = id % CPC;
       if (cl < cols_in && part * ROWS_PER_CHUNK < rows_in) {
         const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
-        *reinterpret_cast<uint4*>(cct + uint32_t(cl) * Ru * CB / 8 + uint32_t(part) * 16) = w;
+        store_nt16(cct + uint32_t(cl) * Ru * CB / 8 + uint32_t(part) * 16, w);
       }
     }
     if (int(threadIdx.x) < cols_in) {
