@@ -65,7 +65,13 @@ def read_counters():
 
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-COPY_BYTES = ALG_BYTES // 2          # each timed torch copy reads and writes this many bytes
+def copy_bytes(alg_bytes: int) -> int:
+    """Bytes each way of the ceiling copy: the workload's read+write byte count,
+    but at least 256 MiB each way so four buffers exceed the 256 MB cache."""
+    return min(max(alg_bytes // 2, 1 << 28), 1 << 31)
+
+
+COPY_BYTES = copy_bytes(ALG_BYTES)   # each ceiling copy of the fused workload reads and writes this much
 CAST_KERNEL = "mx_cast_kernel<true, 0, 0, 3>"
 
 
@@ -329,9 +335,8 @@ def main() -> int:
     del steps_fns
     torch.cuda.empty_cache()
 
-    # a plain device copy as a measured ceiling: the workload's read+write byte
-    # count, but at least 256 MiB each way so four buffers exceed the 256 MB cache
-    copy_half = min(max(alg_bytes // 2, 1 << 28), 1 << 31)
+    # a plain device copy as a measured ceiling
+    copy_half = copy_bytes(alg_bytes)
     src = torch.empty(copy_half, dtype=torch.uint8, device=dev)
     dsts = [torch.empty_like(src) for _ in range(3)]
     for d in dsts:
