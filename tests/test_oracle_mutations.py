@@ -1,0 +1,166 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in the oracle (on the CPU, for the duration of the
+test) and checks that at least one of the pin tests then fails. A pin suite
+that still passed with the mistake in place would not be pinning that part of
+the oracle.
+"""
+import contextlib
+
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.mx_oracle as M
+import test_oracle_dequant as PD
+import test_oracle_encode as PE
+import test_oracle_formats as PF
+import test_oracle_invariants as PI
+import test_oracle_scale as PS
+import test_oracle_worked_example as PW
+
+
+@contextlib.contextmanager
+def planted(name, fn):
+    """Replace oracle function `name` in the module and the package namespace."""
+    old = getattr(M, name)
+    setattr(M, name, fn)
+    setattr(O, name, fn)
+    try:
+        yield
+    finally:
+        setattr(M, name, old)
+        setattr(O, name, old)
+
+
+def fails(check, *args):
+    try:
+        check(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def any_pin_fails(checks):
+    return any(fails(c, *a) for c, a in checks)
+
+
+# ---- planted mistakes ----
+
+def enc_ties_away(s, fmt):
+    """Round half away from zero instead of to even."""
+    codes_pos, vals_pos = M.positive_grid(fmt)
+    a = np.abs(s)
+    idx = np.clip(np.searchsorted(vals_pos, a), 1, len(vals_pos) - 1)
+    lo, hi = idx - 1, idx
+    pick_hi = (vals_pos[hi] - a) <= (a - vals_pos[lo])
+    mag = np.where(pick_hi, codes_pos[hi], codes_pos[lo])
+    mag = np.where(a >= vals_pos[-1], codes_pos[-1], mag)
+    return (mag | (np.signbit(s).astype(np.int64) << (fmt.bits - 1))).astype(np.uint8)
+
+
+def enc_no_saturation(s, fmt):
+    """Overflow becomes the NaN / all-ones code instead of +-max."""
+    c = M._orig_encode(s, fmt)
+    over = np.abs(s) > M.max_finite(fmt)
+    return np.where(over, (c | 0x7F) if fmt.bits == 8 else c, c).astype(np.uint8)
+
+
+def enc_unsigned_zero(s, fmt):
+    """The sign of zero is dropped."""
+    c = M._orig_encode(s, fmt)
+    zero = (s == 0)
+    return np.where(zero, 0, c).astype(np.uint8)
+
+
+def shexp_emax_plus_one(amax, fmt, mode):
+    """The floor rule subtracts emax + 1."""
+    e = M._orig_shexp(amax, fmt, mode)
+    return np.clip(np.where(amax > 0, e - 1, e), -127, 127)
+
+
+def shexp_roundup_ge(amax, fmt, mode):
+    """Round-up rule bumps also when amax equals max * 2^(E - emax) exactly."""
+    amax = np.asarray(amax, dtype=np.float64)
+    if mode != O.ROUNDUP:
+        return M._orig_shexp(amax, fmt, mode)
+    em, vmax = M.emax_of(fmt), M.max_finite(fmt)
+    big_e = np.frexp(amax)[1].astype(np.int64) - 1
+    e = big_e - em + (amax >= np.ldexp(vmax, big_e - em)).astype(np.int64)
+    e = np.where(amax == 0, -127, e)
+    return np.clip(e, -127, 127)
+
+
+def quantize_untransposed(x, in_dtype, fmt, mode, axis):
+    """The column plane keeps X's [B][R][C] element order instead of X^T's."""
+    out = M._orig_quantize(x, in_dtype, fmt, mode, axis)
+    if "col_codes" in out and fmt.bits == 8:
+        cc = out["col_codes"]                                   # [B][C][R]
+        out["col_codes"] = np.ascontiguousarray(cc.transpose(0, 2, 1)).reshape(cc.shape)
+    return out
+
+
+def pack_swapped(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    return ((c[..., 0::2] & 0xF) << 4) | (c[..., 1::2] & 0xF)
+
+
+def dequant_bias_126(codes, scales, fmt, out_dtype):
+    """The E8M0 bias is taken as 126: every scale code reads one step high."""
+    shifted = np.minimum(np.asarray(scales, np.int64) + 1, 254).astype(np.uint8)
+    return M._orig_dequant(codes, shifted, fmt, out_dtype)
+
+
+@pytest.fixture(autouse=True)
+def keep_originals():
+    M._orig_encode = M.encode_elements
+    M._orig_shexp = M.shared_exponent
+    M._orig_quantize = M.quantize
+    M._orig_dequant = M.dequantize
+    yield
+
+
+def test_pins_catch_ties_away_from_zero():
+    with planted("encode_elements", enc_ties_away):
+        assert any_pin_fails([(PE.test_ties_go_to_even_codes, (O.E2M1,)),
+                              (PE.test_encoder_matches_brute_force_scan, (O.E4M3,))])
+
+
+def test_pins_catch_missing_saturation():
+    with planted("encode_elements", enc_no_saturation):
+        assert any_pin_fails([(PE.test_saturation_boundaries, ())])
+
+
+def test_pins_catch_unsigned_zero():
+    with planted("encode_elements", enc_unsigned_zero):
+        assert any_pin_fails([(PE.test_saturation_boundaries, ()),
+                              (PS.test_special_and_zero_blocks, ())])
+
+
+def test_pins_catch_emax_off_by_one():
+    with planted("shared_exponent", shexp_emax_plus_one):
+        assert any_pin_fails([(PS.test_floor_rule_matches_brute_force, (O.E2M1,)),
+                              (PW.test_shared_scale_is_2_pow_minus_4_under_both_rules, ())])
+
+
+def test_pins_catch_roundup_boundary():
+    with planted("shared_exponent", shexp_roundup_ge):
+        assert any_pin_fails([(PS.test_roundup_rule_matches_brute_force, (O.E4M3,)),
+                              (PS.test_landing_intervals, (O.E4M3,))])
+
+
+def test_pins_catch_untransposed_column_plane():
+    with planted("quantize", quantize_untransposed):
+        assert any_pin_fails([(PI.test_column_copy_orientation_closed_form, (O.E4M3,))])
+
+
+def test_pins_catch_swapped_nibbles():
+    with planted("pack_e2m1", pack_swapped):
+        assert any_pin_fails([(PI.test_e2m1_nibble_order, ()),
+                              (PW.test_scaled_values_printed_on_the_page, ())])
+
+
+def test_pins_catch_scale_bias_off_by_one():
+    with planted("dequantize", dequant_bias_126):
+        assert any_pin_fails([(PF.test_e8m0_range_and_nan_scale, ()),
+                              (PD.test_overflow_at_top_of_range_is_inf, ())])
