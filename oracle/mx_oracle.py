@@ -19,16 +19,29 @@ Sources, cited by tag:
 FP8 bit layouts (bias, subnormals, NaN and Inf codes) are not printed on the
 pages; they follow the OCP 8-bit floating-point definitions that [Q] §2 and §8
 refer to, and the tests pin them against torch's float8 types.
+[Q] §2's family table also lists MXFP6 (E2M3 or E3M2, 6.25 bits per element)
+and MXINT8 (INT8, 8.25 bits per element) with the same 32-element blocks and
+E8M0 scale, but prints no bit layout for them; the readings below fill that in.
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * emax of a format is floor(log2(max finite)): 2 (E2M1), 8 (E4M3), 15 (E5M2).
   * FP8 elements use round-to-nearest-even like FP4.
   * Overflow saturates to +-max for every format.
   * A block holding any NaN or +-Inf gets scale 0xFF; its element codes are
-    0x7F (FP8) or 0x0 (E2M1).
+    0x7F (FP8, a NaN code) or 0x0 (formats with no NaN code).
   * An all-zero block gets scale code 0x00 (2^-127); its codes are +-0.
   * Round-up scale rule = the smallest e with amax <= max * 2^e, exactly.
   * E2M1 packing: element 2k in bits 3:0, element 2k+1 in bits 7:4.
+  * E2M3 / E3M2: sign, then 2 / 3 exponent bits with bias 2^(E-1) - 1 (1 / 3),
+    then 3 / 2 mantissa bits, subnormals at exponent field 0, and no Inf or
+    NaN (every code is a number, as in E2M1): maxima 7.5 and 28, emax 2 and 4.
+  * 6-bit packing generalizes the E2M1 nibble order: codes form a little-endian
+    bit stream, element i in stream bits 6i .. 6i+5, byte j holding stream
+    bits 8j .. 8j+7 (4 codes in 3 bytes).
+  * INT8 elements are two's-complement bytes read as k / 64 (the OCP MXINT8
+    element, emax 0, largest value 127/64). Saturation is symmetric: the code
+    -128 (-2.0) is never produced, so encoding keeps code(-x) = -code(x); -0
+    encodes as 0. Formats with no NaN code fill a NaN/Inf block with code 0.
   * The column-wise copy is stored transposed: column-wise(X) = row-wise(X^T).
   * Dequantized values are rounded to the output type with RNE; NaN is written
     as the positive quiet NaN 0x7FC00000 (FP32) or 0x7FC0 (BF16).
@@ -40,10 +53,10 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "Fmt", "E4M3", "E5M2", "E2M1", "FORMATS", "FLOOR", "ROUNDUP", "ROW", "COL", "BOTH",
+    "Fmt", "E4M3", "E5M2", "E2M1", "E2M3", "E3M2", "INT8", "FORMATS", "FLOOR", "ROUNDUP", "ROW", "COL", "BOTH",
     "BLOCK", "decode_code", "value_table", "max_finite", "emax_of", "positive_grid",
     "widen", "encode_elements", "shared_exponent", "quantize_blocks", "quantize",
-    "pack_e2m1", "unpack_e2m1", "dequantize", "round_to_binary", "f32_bits",
+    "pack_e2m1", "unpack_e2m1", "pack_fp6", "unpack_fp6", "pack_codes", "unpack_codes", "dequantize", "round_to_binary", "f32_bits",
     "bf16_bits", "plane_bytes",
 ]
 
@@ -56,17 +69,22 @@ E8M0_NAN = 0xFF        # [Q] §2: 0xFF is NaN, there is no Inf
 
 @dataclass(frozen=True)
 class Fmt:
-    """A sign / exponent / mantissa element format."""
+    """A sign / exponent / mantissa element format, or a fixed-point integer one."""
     name: str
     ebits: int
     mbits: int
     bias: int
     ieee_specials: bool   # E5M2: all-ones exponent holds Inf (m=0) and NaN (m!=0)
     nan_all_ones: bool    # E4M3: only S.1111.111 is NaN, no Inf
+    integer: bool = False  # two's-complement integer; bias = number of fraction bits
 
     @property
     def bits(self) -> int:
         return 1 + self.ebits + self.mbits
+
+    @property
+    def has_nan(self) -> bool:
+        return self.ieee_specials or self.nan_all_ones
 
 
 # [Q] §1: E2M1 = 1 sign, 2 exponent, 1 mantissa bit, no Inf and no NaN.
@@ -76,11 +94,19 @@ E2M1 = Fmt("e2m1", 2, 1, 1, False, False)
 E4M3 = Fmt("e4m3", 4, 3, 7, False, True)
 # [Q] §2 MX family table lists E5M2 as the other MXFP8 element (bias 15, IEEE Inf/NaN).
 E5M2 = Fmt("e5m2", 5, 2, 15, True, False)
-FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
+# [Q] §2 MX family table: MXFP6 takes E2M3 or E3M2 elements (6.25 bits per element).
+E2M3 = Fmt("e2m3", 2, 3, 1, False, False)
+E3M2 = Fmt("e3m2", 3, 2, 3, False, False)
+# [Q] §2 MX family table: MXINT8 (8.25 bits per element); read as k / 2^6.
+INT8 = Fmt("int8", 0, 7, 6, False, False, integer=True)
+FORMATS = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, "e2m3": E2M3, "e3m2": E3M2, "int8": INT8}
 
 
 def decode_code(fmt: Fmt, code: int) -> float:
     """Value of one element code, from the bit definition of the format."""
+    if fmt.integer:
+        k = code - (1 << fmt.bits) if code >> (fmt.bits - 1) else code
+        return k * 2.0 ** -fmt.bias
     sign = -1.0 if (code >> (fmt.bits - 1)) & 1 else 1.0
     exp = (code >> fmt.mbits) & ((1 << fmt.ebits) - 1)
     man = code & ((1 << fmt.mbits) - 1)
@@ -137,7 +163,8 @@ def encode_elements(s: np.ndarray, fmt: Fmt) -> np.ndarray:
     nearest representable value is found in the sorted table; at an exact
     midpoint the neighbour whose code is even wins. [Q] §4: values beyond the
     largest representable magnitude are clipped to it. The sign is copied from
-    s, including the sign of zero.
+    s, including the sign of zero; an integer format negates the magnitude
+    code in two's complement instead (so -0 and +0 share code 0).
     """
     codes_pos, vals_pos = positive_grid(fmt)
     n = len(vals_pos)
@@ -150,6 +177,9 @@ def encode_elements(s: np.ndarray, fmt: Fmt) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes_pos[hi] % 2 == 0))
     mag = np.where(pick_hi, codes_pos[hi], codes_pos[lo])
     mag = np.where(a >= vals_pos[-1], codes_pos[-1], mag)  # saturate at +-max
+    if fmt.integer:
+        neg = np.signbit(s)
+        return np.where(neg, (-mag) & ((1 << fmt.bits) - 1), mag).astype(np.uint8)
     sign = np.signbit(s).astype(np.int64) << (fmt.bits - 1)
     return (mag | sign).astype(np.uint8)
 
@@ -194,7 +224,7 @@ def quantize_blocks(blocks: np.ndarray, fmt: Fmt, mode: int):
     e = shared_exponent(amax, fmt, mode)
     s = np.ldexp(clean, -e[:, None])              # exact: division by a power of two
     codes = encode_elements(s, fmt)
-    codes[special] = 0x7F if fmt.bits == 8 else 0x0
+    codes[special] = 0x7F if fmt.has_nan else 0x0
     scales = (e + E8M0_BIAS).astype(np.uint8)
     scales[special] = E8M0_NAN
     return codes, scales
@@ -214,12 +244,44 @@ def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """Four 6-bit codes per three bytes: the codes, least significant bit first,
+    form one bit stream that is cut into bytes, least significant bit first."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 4 == 0
+    bits = np.unpackbits(c[..., None], axis=-1, bitorder="little")[..., :6]   # [..., N, 6]
+    stream = bits.reshape(c.shape[:-1] + (c.shape[-1] * 6,))
+    return np.packbits(stream, axis=-1, bitorder="little")
+
+
+def unpack_fp6(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    assert p.shape[-1] % 3 == 0
+    stream = np.unpackbits(p, axis=-1, bitorder="little")
+    bits = stream.reshape(p.shape[:-1] + (p.shape[-1] * 8 // 6, 6))
+    return np.packbits(bits, axis=-1, bitorder="little")[..., 0]
+
+
+def pack_codes(codes: np.ndarray, fmt: Fmt) -> np.ndarray:
+    if fmt.bits == 4:
+        return pack_e2m1(codes)
+    if fmt.bits == 6:
+        return pack_fp6(codes)
+    return np.asarray(codes, dtype=np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, fmt: Fmt) -> np.ndarray:
+    if fmt.bits == 4:
+        return unpack_e2m1(packed)
+    if fmt.bits == 6:
+        return unpack_fp6(packed)
+    return np.asarray(packed, dtype=np.uint8)
+
+
 def _quantize_rows(x64: np.ndarray, fmt: Fmt, mode: int):
     b, r, c = x64.shape
     codes, scales = quantize_blocks(x64.reshape(-1, BLOCK), fmt, mode)
-    codes = codes.reshape(b, r, c)
-    if fmt.bits == 4:
-        codes = pack_e2m1(codes)
+    codes = pack_codes(codes.reshape(b, r, c), fmt)
     return codes, scales.reshape(b, r, c // BLOCK)
 
 
@@ -228,7 +290,7 @@ def quantize(x: np.ndarray, in_dtype: str, fmt: Fmt, mode: int, axis: int) -> di
 
     Row blocks are 32 consecutive elements along C; column blocks are 32
     consecutive rows of one column. The column copy is stored transposed,
-    codes [B][C][R] (E2M1: [B][C][R/2]) and scales [B][C][R/32], so that it
+    codes [B][C][R] (E2M1: [B][C][R/2], 6-bit: [B][C][3R/4]) and scales [B][C][R/32], so that it
     equals the row-wise quantization of X^T.
     Returns a dict with the keys row_codes/row_scales and/or col_codes/col_scales.
     """
@@ -282,15 +344,13 @@ def bf16_bits(v: np.ndarray) -> np.ndarray:
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: Fmt, out_dtype: str) -> np.ndarray:
     """Codes + E8M0 scales -> FP32 (uint32 bits) or BF16 (uint16 bits).
 
-    codes: [..., N] (E2M1 packed: [..., N/2]); scales: [..., N/32]. Blocks run
+    codes: [..., N] (packed: E2M1 [..., N/2], 6-bit [..., 3N/4]); scales: [..., N/32]. Blocks run
     along the last axis, so a transposed column plane dequantizes to X^T.
     [Q] §7: applying an E8M0 scale adds to the exponent, with no rounding
     error, so y = value(code) * 2^(k - 127) is formed exactly in float64 and
     rounded once to the output type. [Q] §2: k = 0xFF makes the whole block NaN.
     """
-    c = np.asarray(codes, dtype=np.uint8)
-    if fmt.bits == 4:
-        c = unpack_e2m1(c)
+    c = unpack_codes(codes, fmt)
     k = np.asarray(scales, dtype=np.int64)
     assert c.shape[-1] == k.shape[-1] * BLOCK
     vals = value_table(fmt)[c]

@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 
-FMTS = [O.E4M3, O.E5M2, O.E2M1]
+FMTS = [O.E4M3, O.E5M2, O.E2M1, O.E2M3, O.E3M2, O.INT8]
 
 
 def all_code_scale_pairs(fmt):
@@ -28,7 +28,7 @@ def test_f32_output_is_exact_exponent_add(fmt):
     # "MXFP4 と NVFP4 は何が違うのか調べてみた" §7: applying an E8M0 scale is an
     # exponent add with no rounding error.
     blocks, scales = all_code_scale_pairs(fmt)
-    packed = O.pack_e2m1(blocks) if fmt.bits == 4 else blocks
+    packed = O.pack_codes(blocks, fmt)
     y = O.dequantize(packed, scales, fmt, "f32")[:, 0]
     for code, k, bits in zip(blocks[:, 0], scales[:, 0], y):
         v = O.decode_code(fmt, int(code))
@@ -45,7 +45,7 @@ def test_f32_output_is_exact_exponent_add(fmt):
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
 def test_bf16_output_matches_torch_rounding(fmt):
     blocks, scales = all_code_scale_pairs(fmt)
-    packed = O.pack_e2m1(blocks) if fmt.bits == 4 else blocks
+    packed = O.pack_codes(blocks, fmt)
     f = O.dequantize(packed, scales, fmt, "f32")[:, 0].view(np.float32)
     b = O.dequantize(packed, scales, fmt, "bf16")[:, 0]
     ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

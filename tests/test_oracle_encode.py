@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 
-FMTS = [O.E4M3, O.E5M2, O.E2M1]
+FMTS = [O.E4M3, O.E5M2, O.E2M1, O.E2M3, O.E3M2]   # sign-magnitude formats
 
 
 def brute_code(s: float, fmt) -> int:

@@ -5,7 +5,7 @@ import pytest
 import mx_inputs as I
 import oracle as O
 
-FMTS = [O.E4M3, O.E5M2, O.E2M1]
+FMTS = [O.E4M3, O.E5M2, O.E2M1, O.E2M3, O.E3M2, O.INT8]
 MODES = [O.FLOOR, O.ROUNDUP]
 
 
@@ -22,8 +22,7 @@ def q(x, fmt, mode):
 
 
 def dq(codes, scales, fmt):
-    if fmt.bits == 4:
-        codes = O.pack_e2m1(codes)
+    codes = O.pack_codes(codes, fmt)
     return O.dequantize(codes, scales.reshape(-1, 1), fmt, "f32").view(np.float32).astype(np.float64)
 
 
@@ -50,9 +49,11 @@ def test_sign_symmetry(fmt, mode):
     x = rand_blocks()
     c1, s1 = q(x, fmt, mode)
     c2, s2 = q(-x, fmt, mode)
-    flip = 0x80 if fmt.bits == 8 else 0x8
     assert np.array_equal(s1, s2)
-    assert np.array_equal(c1 ^ flip, c2)
+    if fmt.integer:                                   # two's complement: code(-x) = -code(x)
+        assert np.array_equal((-c1.astype(np.int64)) & 0xFF, c2)
+    else:
+        assert np.array_equal(c1 ^ (1 << (fmt.bits - 1)), c2)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
@@ -77,10 +78,12 @@ def test_error_bound(fmt, mode):
     y = dq(c, s, fmt)
     e = s.astype(np.int64).reshape(-1, 1) - 127
     sv = np.abs(np.ldexp(x, -e))
-    vmin_normal = 2.0 ** (1 - fmt.bias)
+    # INT8 (k / 64) behaves as 6 fraction bits on [1, 2), its top binade
+    m, vmin_normal = (fmt.bias, 1.0) if fmt.integer else (fmt.mbits, 2.0 ** (1 - fmt.bias))
     ok = (sv >= vmin_normal) & (sv <= O.max_finite(fmt))
+    assert ok.sum() > 1000
     rel = np.abs(y - x)[ok] / np.abs(x)[ok]
-    assert rel.max() <= 2.0 ** -(fmt.mbits + 1)
+    assert rel.max() <= 2.0 ** -(m + 1)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)

@@ -15,6 +15,7 @@ import oracle.mx_oracle as M
 import test_oracle_dequant as PD
 import test_oracle_encode as PE
 import test_oracle_formats as PF
+import test_oracle_fp6_int8 as P6
 import test_oracle_invariants as PI
 import test_oracle_scale as PS
 import test_oracle_worked_example as PW
@@ -111,12 +112,35 @@ def dequant_bias_126(codes, scales, fmt, out_dtype):
     return M._orig_dequant(codes, shifted, fmt, out_dtype)
 
 
+def pack_fp6_msb_first(codes):
+    """The 6-bit stream is built most significant bit first."""
+    c = np.asarray(codes, dtype=np.uint8)
+    bits = np.unpackbits(c[..., None], axis=-1)[..., 2:]
+    return np.packbits(bits.reshape(c.shape[:-1] + (c.shape[-1] * 6,)), axis=-1)
+
+
+def enc_int8_sign_magnitude(s, fmt):
+    """INT8 negatives get a sign bit instead of two's complement."""
+    c = M._orig_encode(s, fmt)
+    if not fmt.integer:
+        return c
+    neg = np.signbit(s) & (c != 0)
+    return np.where(neg, ((-c.astype(np.int64)) & 0x7F) | 0x80, c).astype(np.uint8)
+
+
+def decode_e3m2_bias_4(fmt, code):
+    """E3M2 read with bias 4 instead of 3."""
+    v = M._orig_decode(fmt, code)
+    return v / 2.0 if fmt.name == "e3m2" else v
+
+
 @pytest.fixture(autouse=True)
 def keep_originals():
     M._orig_encode = M.encode_elements
     M._orig_shexp = M.shared_exponent
     M._orig_quantize = M.quantize
     M._orig_dequant = M.dequantize
+    M._orig_decode = M.decode_code
     yield
 
 
@@ -164,3 +188,19 @@ def test_pins_catch_scale_bias_off_by_one():
     with planted("dequantize", dequant_bias_126):
         assert any_pin_fails([(PF.test_e8m0_range_and_nan_scale, ()),
                               (PD.test_overflow_at_top_of_range_is_inf, ())])
+
+
+def test_pins_catch_fp6_bit_order():
+    with planted("pack_fp6", pack_fp6_msb_first):
+        assert any_pin_fails([(P6.test_fp6_packing_closed_form, ())])
+
+
+def test_pins_catch_int8_sign_magnitude():
+    with planted("encode_elements", enc_int8_sign_magnitude):
+        assert any_pin_fails([(P6.test_int8_encoder_exhaustive_vs_numpy_rint, ()),
+                              (P6.test_int8_encoder_matches_brute_force_scan, ())])
+
+
+def test_pins_catch_e3m2_bias():
+    with planted("decode_code", decode_e3m2_bias_4):
+        assert any_pin_fails([(P6.test_fp6_tables_are_fp8_low_binades, ("e3m2",))])
