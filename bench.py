@@ -158,15 +158,18 @@ def cpu_baseline(x_gpu, budget_s: float = 12.0):
                       f"E4M3 floor, NumPy float64 oracle, single thread, {t_used:.1f} s"}
 
 
+CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "int8": 8}
+
+
 def _planes(dev, b, r, c, fmt, axis):
     import torch
-    div = 2 if fmt == "e2m1" else 1
+    bits = CODE_BITS[fmt]
     out = {}
     if axis in ("row", "both"):
-        out["row_codes"] = torch.empty((b, r, c // div), dtype=torch.uint8, device=dev)
+        out["row_codes"] = torch.empty((b, r, c * bits // 8), dtype=torch.uint8, device=dev)
         out["row_scales"] = torch.empty((b, r, c // 32), dtype=torch.uint8, device=dev)
     if axis in ("col", "both"):
-        out["col_codes"] = torch.empty((b, c, r // div), dtype=torch.uint8, device=dev)
+        out["col_codes"] = torch.empty((b, c, r * bits // 8), dtype=torch.uint8, device=dev)
         out["col_scales"] = torch.empty((b, c, r // 32), dtype=torch.uint8, device=dev)
     return out
 
@@ -174,7 +177,7 @@ def _planes(dev, b, r, c, fmt, axis):
 def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc):
     """One quantize launch per step over one tensor; bytes = input + code and scale planes."""
     planes = (2 if axis == "both" else 1)
-    nbytes = b * r * c * esize + planes * (b * r * c * (4 if fmt == "e2m1" else 8) // 8 + b * r * c // 32)
+    nbytes = b * r * c * esize + planes * (b * r * c * CODE_BITS[fmt] // 8 + b * r * c // 32)
 
     def make(dev, i):
         import microscaling_block_quantized_amd as mx
@@ -263,6 +266,12 @@ WORKLOADS = {
                                       "weights 14336x4096 bf16 -> MXFP4 E2M1 row-wise, round-up scale rule"),
     "gradients": _cast_workload(_gen("gradients"), 1, 8192, 8192, 4, "e5m2", "roundup", "col",
                                 "gradients 8192x8192 fp32 -> MXFP8 E5M2 column-wise, round-up scale rule"),
+    "act_e2m3": _cast_workload(_gen("activations"), 1, ROWS, COLS, 2, "e2m3", "floor", "both",
+                               "activations 16384x4096 bf16 -> MXFP6 E2M3 row+col fused, floor scale rule"),
+    "act_e3m2": _cast_workload(_gen("activations"), 1, ROWS, COLS, 2, "e3m2", "floor", "both",
+                               "activations 16384x4096 bf16 -> MXFP6 E3M2 row+col fused, floor scale rule"),
+    "act_int8": _cast_workload(_gen("activations"), 1, ROWS, COLS, 2, "int8", "floor", "both",
+                               "activations 16384x4096 bf16 -> MXINT8 row+col fused, floor scale rule"),
     "wide_range": _wide_range_pipeline(),
     "fp32_normal": _fp32_normal_round_trip(),
 }

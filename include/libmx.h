@@ -39,17 +39,28 @@ extern "C" {
 
 /* Element formats. E4M3: bias 7, max 448, no Inf, NaN = S.1111.111.
  * E5M2: bias 15, max 57344, IEEE Inf/NaN. E2M1: bias 1, values
- * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, no Inf/NaN. */
-typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 } mx_fmt;
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, no Inf/NaN.
+ * The other rows of the same article's §2 family table (MXFP6, 6.25 bits per
+ * element; MXINT8, 8.25), read as the OCP elements:
+ * E2M3: sign in bit 5, 2 exponent bits (bias 1), 3 mantissa bits, max 7.5;
+ * E3M2: sign in bit 5, 3 exponent bits (bias 3), 2 mantissa bits, max 28;
+ *       both with subnormals and without Inf/NaN; 4 codes per 3 bytes, the
+ *       codes forming a little-endian bit stream (element i in bits 6i..6i+5);
+ * INT8: two's-complement k meaning k/64 (max 127/64, emax 0), rounded to
+ *       nearest-even and clipped to +-127 (-128 is never produced). */
+typedef enum {
+  MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2, MX_E2M3 = 3, MX_E3M2 = 4, MX_INT8 = 5
+} mx_fmt;
 
 /* Shared-exponent rules (same article, §4 and the rounding paragraph of §2):
  * MX_SCALE_FLOOR   e = floor(log2(amax)) - emax (OCP example rule; the scaled
  *                  block max lands in [2^emax, 2^(emax+1)), the excess clips);
  * MX_SCALE_ROUNDUP the smallest e with amax <= max * 2^e (no clipping; the
  *                  scaled block max lands in (max/2, max]).
- * emax = floor(log2(max)): 8 (E4M3), 15 (E5M2), 2 (E2M1). e is clamped to
- * [-127, 127]; an all-zero block gets code 0x00. A block holding a NaN or an
- * Inf gets scale 0xFF and element codes 0x7F (FP8) or 0x0 (E2M1). */
+ * emax = floor(log2(max)): 8 (E4M3), 15 (E5M2), 2 (E2M1, E2M3), 4 (E3M2),
+ * 0 (INT8). e is clamped to [-127, 127]; an all-zero block gets code 0x00. A
+ * block holding a NaN or an Inf gets scale 0xFF and element codes 0x7F (FP8)
+ * or 0x0 (formats with no NaN code). */
 typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_ROUNDUP = 1 } mx_scale_mode;
 
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
@@ -73,16 +84,19 @@ typedef struct {
 #define MX_ERR_LAUNCH (-7)      /* the kernel launch failed (hipGetLastError) */
 
 /* Bytes of ONE code plane and ONE scale plane for a tensor of shape s quantized
- * to fmt (both axes have the same sizes): code = batch*rows*cols*bits/8,
+ * to fmt (both axes have the same sizes): code = batch*rows*cols*bits/8 (bits
+ * 8, 6 or 4),
  * scale = batch*rows*cols/32. Shape rules are those of mx_quantize with
  * MX_AXIS_BOTH. Pure host arithmetic; no HIP call. */
 int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_bytes);
 
 /* Quantize x ([batch][rows][cols], x_dtype) into the planes selected by axis.
  *   row_codes  [batch][rows][cols] bytes, E2M1: [batch][rows][cols/2] with
- *              element 2k in bits 3:0 and element 2k+1 in bits 7:4
+ *              element 2k in bits 3:0 and element 2k+1 in bits 7:4,
+ *              E2M3/E3M2: [batch][rows][3*cols/4]
  *   row_scales [batch][rows][cols/32] E8M0 bytes
- *   col_codes  [batch][cols][rows] bytes, E2M1: [batch][cols][rows/2]
+ *   col_codes  [batch][cols][rows] bytes, E2M1: [batch][cols][rows/2],
+ *              E2M3/E3M2: [batch][cols][3*rows/4]
  *   col_scales [batch][cols][rows/32]
  * Pointers of an axis not in `axis` must be NULL; the others must be non-NULL.
  * Shape: batch, rows, cols >= 1; cols % 32 == 0 always (16-byte vector rows);
@@ -94,12 +108,12 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
 
 /* Dequantize one plane. s is the shape of the plane as stored, with blocks of
  * 32 along s.cols (a column plane is passed as [batch][cols][rows] and comes
- * out as X^T). codes: batch*rows*cols bytes (E2M1: half); scales:
- * batch*rows*cols/32 bytes; y: batch*rows*cols elements of y_dtype. FP32
- * output is exact; BF16 output is the exact value rounded to nearest-even.
- * NaN is written as 0x7FC00000 (FP32) / 0x7FC0 (BF16).
- * Shape: extents >= 1, cols % 32 == 0. codes and y 16-byte aligned (E2M1
- * codes 8-byte aligned). y must not overlap codes or scales. */
+ * out as X^T). codes: batch*rows*cols bytes (E2M1: half, E2M3/E3M2: three
+ * quarters); scales: batch*rows*cols/32 bytes; y: batch*rows*cols elements of
+ * y_dtype. FP32 output is exact; BF16 output is the exact value rounded to
+ * nearest-even. NaN is written as 0x7FC00000 (FP32) / 0x7FC0 (BF16).
+ * Shape: extents >= 1, cols % 32 == 0. y 16-byte aligned; codes 16-byte
+ * aligned (E2M1 8-byte, E2M3/E3M2 4-byte). y must not overlap codes or scales. */
 int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s,
                   mx_dtype y_dtype, void* y, void* stream);
 

@@ -18,11 +18,12 @@ import ctypes
 import os
 
 __all__ = [
-    "MXError", "FMT", "MODE", "AXIS", "DTYPE", "lib_path", "load", "mx_version", "mx_strerror",
+    "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "lib_path", "load", "mx_version", "mx_strerror",
     "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize", "BoundDequantize",
 ]
 
-FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4, "int8": 5}
+CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "int8": 8}
 MODE = {"floor": 0, "roundup": 1}
 AXIS = {"row": 1, "col": 2, "both": 3}
 DTYPE = {"f32": 0, "bf16": 1}
@@ -111,8 +112,9 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
 
     Returns {"row_codes", "row_scales"} and/or {"col_codes", "col_scales"} as
     uint8 tensors: row planes [B][R][C'] / [B][R][C/32], column planes
-    [B][C][R'] / [B][C][R/32] (C' = C, or C/2 packed for e2m1); the batch axis
-    is dropped for a 2-D input. ``out`` may supply preallocated planes.
+    [B][C][R'] / [B][C][R/32] (C' = C * code bits / 8: C for the 8-bit
+    formats, 3C/4 for e2m3 / e3m2, C/2 for e2m1); the batch axis is dropped
+    for a 2-D input. ``out`` may supply preallocated planes.
     """
     import torch
     if not x.is_cuda:
@@ -124,7 +126,7 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
     b, r, c = _shape3(x.shape)
     squeeze = x.dim() == 2
     ax = AXIS[axis]
-    div = 2 if fmt == "e2m1" else 1
+    bits = CODE_BITS[fmt]
     out = out or {}
     dev = x.device
 
@@ -134,10 +136,10 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
 
     planes = {}
     if ax & 1:
-        planes["row_codes"] = plane("row_codes", (b, r, c // div))
+        planes["row_codes"] = plane("row_codes", (b, r, c * bits // 8))
         planes["row_scales"] = plane("row_scales", (b, r, c // 32))
     if ax & 2:
-        planes["col_codes"] = plane("col_codes", (b, c, r // div))
+        planes["col_codes"] = plane("col_codes", (b, c, r * bits // 8))
         planes["col_scales"] = plane("col_scales", (b, c, max(r // 32, 1)))
     with torch.cuda.device(dev):
         err = load().mx_quantize(

@@ -13,12 +13,16 @@ namespace {
 constexpr int64_t kBlock = 32;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
-bool valid_fmt(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
+bool valid_fmt(int f) {
+  return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1 || f == MX_E2M3 || f == MX_E3M2 || f == MX_INT8;
+}
 bool valid_mode(int m) { return m == MX_SCALE_FLOOR || m == MX_SCALE_ROUNDUP; }
 bool valid_dtype(int d) { return d == MX_F32 || d == MX_BF16; }
 bool valid_axis(int a) { return a == MX_AXIS_ROW || a == MX_AXIS_COL || a == MX_AXIS_BOTH; }
 
-int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : 8; }
+int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : (fmt == MX_E2M3 || fmt == MX_E3M2) ? 6 : 8; }
+// dequantize reads 16 codes per thread: 16, 12 or 8 bytes
+uintptr_t dequant_code_align(int fmt) { return fmt == MX_E2M1 ? 8 : code_bits(fmt) == 6 ? 4 : 16; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -49,7 +53,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10000; }
+int mx_version(void) { return 10100; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -136,7 +140,7 @@ int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape
   if (codes == nullptr || scales == nullptr || y == nullptr) return MX_ERR_NULL;
   const int64_t n = elements(s);
   if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
-  if (!aligned(codes, fmt == MX_E2M1 ? 8 : 16) || !aligned(y, 16)) return MX_ERR_ALIGN;
+  if (!aligned(codes, dequant_code_align(fmt)) || !aligned(y, 16)) return MX_ERR_ALIGN;
   const Range rc = range_of(codes, n / 8 * code_bits(fmt));
   const Range rsc = range_of(scales, n / kBlock);
   const Range ry = range_of(y, n * (y_dtype == MX_BF16 ? 2 : 4));

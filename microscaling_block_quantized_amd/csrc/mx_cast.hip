@@ -57,6 +57,14 @@ __device__ __forceinline__ void store_nt8(void* p, uint2 v) {
 __device__ __forceinline__ void store_nt4(void* p, uint32_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
+// Three dword stores to consecutive addresses; the compiler merges them into
+// one 12-byte store (global_store_dwordx3), which needs only 4-byte alignment.
+__device__ __forceinline__ void store_nt12(void* p, uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+  __builtin_nontemporal_store(a, q);
+  __builtin_nontemporal_store(b, q + 1);
+  __builtin_nontemporal_store(c, q + 2);
+}
 __device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
   __builtin_nontemporal_store(static_cast<unsigned short>(v), reinterpret_cast<unsigned short*>(p));
 }
@@ -89,10 +97,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   constexpr int RG = 64 / LPR;                 // row groups per wave: 4 | 2
   constexpr int RPT = 32 / RG;                 // rows per thread: 8 | 16
   constexpr int LPB = 32 / VEC;                // lanes per row block: 4 | 8
-  constexpr int CB = FmtC<F>::bits;            // code bits
+  constexpr int CB = FmtC<F>::bits;            // code bits in memory: 8 | 6 | 4
+  constexpr int RB = kRegBits<F>;              // code bits as formed and staged: 8 | 4
   constexpr bool ROWS = (AX & kRow) != 0;
   constexpr bool COLS = (AX & kCol) != 0;
-  constexpr int BPC = kTileR * CB / 8;         // staged code bytes per tile column: 128 | 64
+  constexpr int BPC = kTileR * RB / 8;         // staged code bytes per tile column: 128 | 64
   constexpr int CPC = BPC / 16;                // 16-byte chunks per staged column: 8 | 4
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
@@ -189,14 +198,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu * CB / 8;
       if constexpr (BF16) {
         const uint2 w = encode8_bf16<F, M>(v[k].x, v[k].y, v[k].z, v[k].w, code);
-        if (ok) {
+        if constexpr (CB == 6) {
+          // 48 bits per lane: even lanes store theirs and the odd neighbour's as 12 bytes
+          const uint32_t hi = pack6(w.y);
+          const uint32_t e0 = pack6(w.x) | (hi << 24), e1 = hi >> 8;
+          const uint32_t o0 = dpp<kDppXor1>(e0), o1 = dpp<kDppXor1>(e1);
+          if (ok && (t & 1) == 0) store_nt12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+        } else if (ok) {
           if constexpr (CB == 8) store_nt8(dst, w);
           else store_nt4(dst, w.x);
         }
       } else {
         const uint32_t w = encode4_f32<F, M>(__uint_as_float(v[k].x), __uint_as_float(v[k].y),
                                              __uint_as_float(v[k].z), __uint_as_float(v[k].w), code);
-        if (ok) {
+        if constexpr (CB == 6) {
+          // 24 bits per lane: lane 4i stores the 12 bytes of lanes 4i .. 4i+3
+          const uint32_t g0 = pack6(w);
+          const uint32_t g1 = dpp<kDppQuadNext>(g0), g2 = dpp<kDppXor2>(g0), g3 = dpp<kDppQuadPrev>(g0);
+          if (ok && (t & 3) == 0) store_nt12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+        } else if (ok) {
           if constexpr (CB == 8) store_nt4(dst, w);
           else store_nt2(dst, w);
         }
@@ -229,7 +249,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   if constexpr (COLS) {
     // encode column j of this thread (rows lrow .. +RPT-1) and stage it at
     // [column][row], the 16-byte chunk index XORed with (column / 8) mod CPC
-    const int byte0 = lrow * CB / 8;                  // this thread's offset inside a staged column
+    const int byte0 = lrow * RB / 8;                  // this thread's offset inside a staged column
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
       const int cl = lcol + j;
@@ -241,7 +261,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 #pragma unroll
         for (int k = 0; k < RPT; k += 2) pr[k / 2] = __builtin_amdgcn_perm((&v[k + 1].x)[d], (&v[k].x)[d], sel);
         const uint2 w = encode8_bf16<F, M>(pr[0], pr[1], pr[2], pr[3], code_j[j]);
-        if constexpr (CB == 8) *reinterpret_cast<uint2*>(lds_codes + off) = w;       // 8 rows
+        if constexpr (RB == 8) *reinterpret_cast<uint2*>(lds_codes + off) = w;       // 8 rows
         else *reinterpret_cast<uint32_t*>(lds_codes + off) = w.x;                   // 8 rows in 4 bytes
       } else {
         uint32_t w[RPT / 4];
@@ -250,7 +270,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
           w[g] = encode4_f32<F, M>(__uint_as_float((&v[4 * g].x)[j]), __uint_as_float((&v[4 * g + 1].x)[j]),
                                    __uint_as_float((&v[4 * g + 2].x)[j]), __uint_as_float((&v[4 * g + 3].x)[j]),
                                    code_j[j]);
-        if constexpr (CB == 8) {
+        if constexpr (RB == 8) {
           *reinterpret_cast<uint4*>(lds_codes + off) = make_uint4(w[0], w[1], w[2], w[3]);   // 16 rows
         } else {
           *reinterpret_cast<uint2*>(lds_codes + off) =
@@ -264,9 +284,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     }
     __syncthreads();
 
-    // transposed write-out: tile column cl -> row (c0 + cl) of the column plane
-    constexpr int ROWS_PER_CHUNK = 16 * 8 / CB;
+    // transposed write-out: tile column cl -> row (c0 + cl) of the column plane;
+    // 16 staged bytes (ROWS_PER_CHUNK rows) go out as 16 bytes, or 12 once packed to 6 bits
+    constexpr int ROWS_PER_CHUNK = 16 * 8 / RB;
+    constexpr uint32_t OUT_CHUNK = 16 * CB / RB;
     const uint32_t Ru = uint32_t(R);
+    const uint32_t cpitch = Ru * CB / 8;              // column-plane row pitch in bytes (< 2^23)
     const int64_t ctile_elem = (int64_t(bi) * C + c0) * R + r0;
     uint8_t* cct = reinterpret_cast<uint8_t*>(a.col_codes) + ctile_elem * CB / 8;
 #pragma unroll
@@ -276,7 +299,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int part = id % CPC;
       if (cl < cols_in && part * ROWS_PER_CHUNK < rows_in) {
         const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
-        store_nt16(cct + uint32_t(cl) * Ru * CB / 8 + uint32_t(part) * 16, w);
+        uint8_t* dst = cct + uint32_t(cl) * cpitch + uint32_t(part) * OUT_CHUNK;
+        if constexpr (CB == 6) {
+          const uint3 p = pack6x16(w.x, w.y, w.z, w.w);
+          store_nt12(dst, p.x, p.y, p.z);
+        } else {
+          store_nt16(dst, w);
+        }
       }
     }
     if (int(threadIdx.x) < cols_in) {
@@ -336,18 +365,31 @@ __global__ __launch_bounds__(kRowThreads) void mx_cast_rows_kernel(CastArgs a, i
     m = group_max<LPB>(m);
     const uint32_t code = scale_code<F, M, BF16>(m);
     const int64_t e0 = ch * VEC;                       // first element of this chunk
+    uint8_t* dst = rc + e0 * CB / 8;
     if constexpr (BF16) {
       const uint2 w = encode8_bf16<F, M>(v[u].x, v[u].y, v[u].z, v[u].w, code);
-      if (ch < nchunks) {
-        if constexpr (CB == 8) store_nt8(rc + e0, w);
-        else store_nt4(rc + e0 / 2, w.x);
+      if constexpr (CB == 6) {
+        // even lanes store their 48 bits and the odd neighbour's as 12 bytes
+        const uint32_t hi = pack6(w.y);
+        const uint32_t p0 = pack6(w.x) | (hi << 24), p1 = hi >> 8;
+        const uint32_t o0 = dpp<kDppXor1>(p0), o1 = dpp<kDppXor1>(p1);
+        if (ch < nchunks && (lane & 1) == 0) store_nt12(dst, p0, p1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+      } else if (ch < nchunks) {
+        if constexpr (CB == 8) store_nt8(dst, w);
+        else store_nt4(dst, w.x);
       }
     } else {
       const uint32_t w = encode4_f32<F, M>(__uint_as_float(v[u].x), __uint_as_float(v[u].y),
                                            __uint_as_float(v[u].z), __uint_as_float(v[u].w), code);
-      if (ch < nchunks) {
-        if constexpr (CB == 8) store_nt4(rc + e0, w);
-        else store_nt2(rc + e0 / 2, w);
+      if constexpr (CB == 6) {
+        // lane 4i stores the 24 bits of lanes 4i .. 4i+3 as 12 bytes
+        const uint32_t g0 = pack6(w);
+        const uint32_t g1 = dpp<kDppQuadNext>(g0), g2 = dpp<kDppXor2>(g0), g3 = dpp<kDppQuadPrev>(g0);
+        if (ch < nchunks && (lane & 3) == 0)
+          store_nt12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+      } else if (ch < nchunks) {
+        if constexpr (CB == 8) store_nt4(dst, w);
+        else store_nt2(dst, w);
       }
     }
     // scale bytes of the 4 blocks of this lane's group, lane 0 of the group stores
@@ -407,7 +449,11 @@ hipError_t by_fmt(int fmt, int mode, int axis, const CastArgs& a, uint32_t nb, h
   switch (fmt) {
     case kE4M3: return by_mode<BF16, kE4M3>(mode, axis, a, nb, s);
     case kE5M2: return by_mode<BF16, kE5M2>(mode, axis, a, nb, s);
-    default: return by_mode<BF16, kE2M1>(mode, axis, a, nb, s);
+    case kE2M1: return by_mode<BF16, kE2M1>(mode, axis, a, nb, s);
+    case kE2M3: return by_mode<BF16, kE2M3>(mode, axis, a, nb, s);
+    case kE3M2: return by_mode<BF16, kE3M2>(mode, axis, a, nb, s);
+    case kInt8: return by_mode<BF16, kInt8>(mode, axis, a, nb, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

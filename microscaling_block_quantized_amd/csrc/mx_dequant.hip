@@ -7,8 +7,13 @@
 // included) by the gfx950 scaled up-conversion, and BF16 output is that FP32
 // rounded to nearest-even. NaN is written as the positive quiet NaN.
 //
-// One thread handles 16 consecutive elements (half a block): a 16-byte (FP8)
-// or 8-byte (E2M1) code load, one scale byte, and 64 or 32 bytes of output.
+// E2M3 / E3M2 codes are decoded as their FP8 carrier (E4M3 / E5M2, the same
+// values 2^6 / 2^12 lower, see mx_device.h) and multiplied back up, exactly.
+// INT8 code k is the value (k ^ 0x80) - 128 in units of 2^(scale - 133).
+//
+// One thread handles 16 consecutive elements (half a block): a 16-byte (FP8,
+// INT8), 12-byte (FP6) or 8-byte (E2M1) code load, one scale byte, and 64 or
+// 32 bytes of output.
 #include "mx_kernels.h"
 
 namespace mx {
@@ -36,9 +41,42 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Two FP8 codes (lo or hi half of c) times the scale, in element order.
 template <int F>
-__device__ __forceinline__ void decode16(const uint32_t* cw, float sc, float* o) {
-  if constexpr (F == kE2M1) {
+__device__ __forceinline__ float2v fp8_pair(uint32_t c, float sc, bool hi) {
+  if constexpr (F == kE4M3) return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, sc, true)
+                                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, sc, false);
+  else return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(c, sc, true)
+                 : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(c, sc, false);
+}
+
+template <int F>
+__device__ __forceinline__ void decode16(const uint32_t* cw, uint32_t k, float* o) {
+  const float sc = scale_operand(k);
+  if constexpr (kIsFp6<F>) {
+    // 12 bytes -> four 24-bit groups of 4 codes -> carrier bytes (sign from bit 5 to bit 7)
+    constexpr int CF = FmtC<F>::carrier;
+    const float up = __uint_as_float(uint32_t(127 + FmtC<F>::shift) << 23);
+    const uint32_t g[4] = {cw[0], (cw[0] >> 24) | (cw[1] << 8), (cw[1] >> 16) | (cw[2] << 16), cw[2] >> 8};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t c6 = unpack6(g[d]);
+      const uint32_t c8 = (c6 & 0x1F1F1F1Fu) | ((c6 & 0x20202020u) << 2);
+      const float2v lo = fp8_pair<CF>(c8, sc, false), hi = fp8_pair<CF>(c8, sc, true);
+      o[4 * d + 0] = lo.x * up; o[4 * d + 1] = lo.y * up; o[4 * d + 2] = hi.x * up; o[4 * d + 3] = hi.y * up;
+    }
+  } else if constexpr (F == kInt8) {
+    // unit 2^(k-133): an FP32 normal for k >= 7, else the subnormal with bit k+16 set;
+    // the integer (exact in FP32) times the unit is exact, or overflows only when
+    // the value itself does
+    const float unit = __uint_as_float(k >= 7u ? (k - 6u) << 23 : 1u << (k + 16u));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t u = cw[d] ^ 0x80808080u;          // offset binary: byte = k + 128
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[4 * d + b] = (float((u >> (8 * b)) & 0xFFu) - 128.0f) * unit;
+    }
+  } else if constexpr (F == kE2M1) {
     // two dwords hold 16 codes, element 2k in the low nibble of byte k
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -52,14 +90,7 @@ __device__ __forceinline__ void decode16(const uint32_t* cw, float sc, float* o)
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      float2v lo, hi;
-      if constexpr (F == kE4M3) {
-        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[d], sc, false);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[d], sc, true);
-      } else {
-        lo = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(cw[d], sc, false);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(cw[d], sc, true);
-      }
+      const float2v lo = fp8_pair<F>(cw[d], sc, false), hi = fp8_pair<F>(cw[d], sc, true);
       o[4 * d + 0] = lo.x; o[4 * d + 1] = lo.y; o[4 * d + 2] = hi.x; o[4 * d + 3] = hi.y;
     }
   }
@@ -76,12 +107,19 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
   if constexpr (F == kE2M1) {
     const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(codes + i * 8));
     cw[0] = c.x; cw[1] = c.y; cw[2] = 0; cw[3] = 0;
+  } else if constexpr (kIsFp6<F>) {
+    // three dword loads of consecutive addresses, merged into one 12-byte load
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(codes + i * 12);
+    cw[0] = __builtin_nontemporal_load(q);
+    cw[1] = __builtin_nontemporal_load(q + 1);
+    cw[2] = __builtin_nontemporal_load(q + 2);
+    cw[3] = 0;
   } else {
     const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + i * 16));
     cw[0] = c.x; cw[1] = c.y; cw[2] = c.z; cw[3] = c.w;
   }
   float o[16];
-  decode16<F>(cw, scale_operand(k), o);
+  decode16<F>(cw, k, o);
   uint32_t ob[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e)
@@ -116,17 +154,23 @@ hipError_t launch_dq(const uint8_t* c, const uint8_t* s, void* y, int64_t n, hip
   return hipGetLastError();
 }
 
+template <int F>
+hipError_t by_out(bool out_bf16, const uint8_t* c, const uint8_t* s, void* y, int64_t n, hipStream_t st) {
+  return out_bf16 ? launch_dq<F, true>(c, s, y, n, st) : launch_dq<F, false>(c, s, y, n, st);
+}
+
 }  // namespace
 
 hipError_t launch_dequant(int fmt, bool out_bf16, const uint8_t* codes, const uint8_t* scales,
                           void* y, int64_t n, hipStream_t s) {
   switch (fmt) {
-    case kE4M3: return out_bf16 ? launch_dq<kE4M3, true>(codes, scales, y, n, s)
-                                : launch_dq<kE4M3, false>(codes, scales, y, n, s);
-    case kE5M2: return out_bf16 ? launch_dq<kE5M2, true>(codes, scales, y, n, s)
-                                : launch_dq<kE5M2, false>(codes, scales, y, n, s);
-    default: return out_bf16 ? launch_dq<kE2M1, true>(codes, scales, y, n, s)
-                             : launch_dq<kE2M1, false>(codes, scales, y, n, s);
+    case kE4M3: return by_out<kE4M3>(out_bf16, codes, scales, y, n, s);
+    case kE5M2: return by_out<kE5M2>(out_bf16, codes, scales, y, n, s);
+    case kE2M1: return by_out<kE2M1>(out_bf16, codes, scales, y, n, s);
+    case kE2M3: return by_out<kE2M3>(out_bf16, codes, scales, y, n, s);
+    case kE3M2: return by_out<kE3M2>(out_bf16, codes, scales, y, n, s);
+    case kInt8: return by_out<kInt8>(out_bf16, codes, scales, y, n, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

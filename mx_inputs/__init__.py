@@ -33,7 +33,10 @@ __all__ = [
 
 # Largest finite element magnitude and its binade, used only to place anchor
 # values when arranging the sweep inputs.
-FMT_MAX = {"e4m3": (448.0, 8), "e5m2": (57344.0, 15), "e2m1": (6.0, 2)}
+FMT_MAX = {"e4m3": (448.0, 8), "e5m2": (57344.0, 15), "e2m1": (6.0, 2), "e2m3": (7.5, 2),
+           "e3m2": (28.0, 4), "int8": (127 / 64, 0)}
+# (mantissa bits, bias) of the sign/exponent/mantissa formats, for placing probes
+_FP_LAYOUT = {"e4m3": (3, 7), "e5m2": (2, 15), "e2m3": (3, 1), "e3m2": (2, 3)}
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -189,10 +192,12 @@ def fp32_edges(fmt: str) -> torch.Tensor:
     # code grid of the element format (magnitudes), built from its bit layout
     if fmt == "e2m1":
         grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    elif fmt == "int8":
+        grid = [k / 64.0 for k in range(128)]
     else:
-        mb, bias = (3, 7) if fmt == "e4m3" else (2, 15)
+        mb, bias = _FP_LAYOUT[fmt]
         grid = []
-        for code in range(0, 1 << (7)):
+        for code in range(0, 1 << 7):
             ex, man = code >> mb, code & ((1 << mb) - 1)
             val = (man / (1 << mb)) * 2.0 ** (1 - bias) if ex == 0 else (1 + man / (1 << mb)) * 2.0 ** (ex - bias)
             if val <= vmax:
@@ -222,6 +227,10 @@ def fp32_edges(fmt: str) -> torch.Tensor:
     blocks.append(sub + [0.0] * (32 - len(sub)))
     blocks.append([2.0 ** -126] + sub + [-0.0] * (31 - len(sub)))
     blocks.append([1.0] + sub + [2.0 ** -10 * k for k in range(25)])
+    # subnormal block maxima whose mantissa field sits around 0x7E0000 and 0x7F0000
+    for mant in (0x7E0000, 0x7E0001, 0x7F0000, 0x7F0001, 0x7FFFFF):
+        amax = mant * 2.0 ** -149
+        blocks.append([amax, -amax] + [amax * k / 32 for k in range(30)])
     # tiny normal maxima around the scale clamp (round-up edge included)
     t = torch.tensor(1.75 * 2.0 ** -119, dtype=torch.float32)
     tn = torch.nextafter(t, _f32(math.inf)).item()

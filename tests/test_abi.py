@@ -36,16 +36,17 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10000
+    assert mxb.mx_version() == 10100
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
     assert mxb.mx_strerror(-99) == "unknown libmx error"
 
 
-@pytest.mark.parametrize("fmt,bpe", [("e4m3", 8.25), ("e5m2", 8.25), ("e2m1", 4.25)])
+@pytest.mark.parametrize("fmt,bpe", [("e4m3", 8.25), ("e5m2", 8.25), ("e2m1", 4.25), ("e2m3", 6.25),
+                                     ("e3m2", 6.25), ("int8", 8.25)])
 def test_plane_bytes(fmt, bpe):
-    # "MXFP4 と NVFP4 は何が違うのか調べてみた" §2: 4.25 / 8.25 bits per element
+    # "MXFP4 と NVFP4 は何が違うのか調べてみた" §2: 4.25 / 6.25 / 8.25 bits per element
     for shape in [(16384, 4096), (14336, 4096), (64, 4096, 14336), (1, 32)]:
         cb, sb = mxb.mx_plane_bytes(fmt, shape)
         n = 1
@@ -74,7 +75,8 @@ def q(lib, x=X, dt=1, shape=(1, 64, 64), fmt=0, mode=0, axis=3, rc=RC, rs=RS, cc
 
 
 def test_quantize_argument_errors(lib):
-    assert q(lib, fmt=3) == E_ENUM
+    assert q(lib, fmt=6) == E_ENUM
+    assert q(lib, fmt=-1) == E_ENUM
     assert q(lib, mode=2) == E_ENUM
     assert q(lib, dt=2) == E_ENUM
     assert q(lib, axis=0) == E_ENUM
@@ -107,6 +109,9 @@ def test_dequantize_argument_errors(lib):
     assert dq(shape=(1, 64, 40)) == E_SHAPE
     assert dq(shape=(1, 0, 64)) == E_SHAPE
     assert dq(c=CC + 8) == E_ALIGN
+    assert dq(c=CC + 4, fmt=2) == E_ALIGN                # E2M1 codes: 8-byte aligned
+    assert dq(c=CC + 2, fmt=3) == E_ALIGN                # E2M3 codes: 4-byte aligned
+    assert dq(c=CC + 8, fmt=5) == E_ALIGN                # INT8 codes: 16-byte aligned
     assert dq(y=Y + 4) == E_ALIGN
     assert dq(y=CC + 16) == E_ALIAS
 

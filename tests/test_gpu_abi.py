@@ -18,16 +18,19 @@ def guarded(nbytes):
     return buf, buf[GUARD:GUARD + nbytes]
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
-@pytest.mark.parametrize("shape", [(160, 96), (2, 96, 224), (1, 33, 64)])
+OFMT = {"e4m3": O.E4M3, "e2m1": O.E2M1, "e2m3": O.E2M3, "e3m2": O.E3M2, "int8": O.INT8}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "e2m3", "e3m2", "int8"])
+@pytest.mark.parametrize("shape", [(160, 96), (2, 96, 224), (1, 33, 64), (64, 32)])
 def test_writes_stay_inside_outputs(mx, fmt, shape):
     """Every output plane sits between 4 KiB canary bands that must survive."""
     x = torch.randn(shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
     b, r, c = (1,) + tuple(shape) if len(shape) == 2 else shape
     axis = "both" if r % 32 == 0 else "row"
-    div = 2 if fmt == "e2m1" else 1
-    sizes = {"row_codes": (b, r, c // div), "row_scales": (b, r, c // 32),
-             "col_codes": (b, c, r // div), "col_scales": (b, c, max(r // 32, 1))}
+    bits = OFMT[fmt].bits
+    sizes = {"row_codes": (b, r, c * bits // 8), "row_scales": (b, r, c // 32),
+             "col_codes": (b, c, r * bits // 8), "col_scales": (b, c, max(r // 32, 1))}
     keys = ["row_codes", "row_scales"] + (["col_codes", "col_scales"] if axis == "both" else [])
     bufs, out = {}, {}
     for k in keys:
@@ -36,7 +39,7 @@ def test_writes_stay_inside_outputs(mx, fmt, shape):
         out[k] = view.view(sizes[k])
     mx.mx_quantize(x.view(b, r, c), fmt, "floor", axis, out=out)
     torch.cuda.synchronize()
-    ref = O.quantize(I.to_bits(x.view(b, r, c).cpu()), "bf16", {"e4m3": O.E4M3, "e2m1": O.E2M1}[fmt],
+    ref = O.quantize(I.to_bits(x.view(b, r, c).cpu()), "bf16", OFMT[fmt],
                      O.FLOOR, O.BOTH if axis == "both" else O.ROW)
     for k in keys:
         buf = bufs[k].cpu().numpy()
@@ -44,15 +47,21 @@ def test_writes_stay_inside_outputs(mx, fmt, shape):
         assert np.array_equal(out[k].cpu().numpy(), ref[k]), k
 
 
-def test_dequant_writes_stay_inside_output(mx):
-    codes = torch.randint(0, 256, (96, 64), dtype=torch.uint8, generator=torch.Generator().manual_seed(1)).cuda()
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m3"])
+def test_dequant_writes_stay_inside_output(mx, fmt):
+    nbytes = 64 * OFMT[fmt].bits // 8
+    codes = torch.randint(0, 256, (96, nbytes), dtype=torch.uint8, generator=torch.Generator().manual_seed(1))
+    cbuf, cview = guarded(96 * nbytes)               # codes end right at a canary band
+    cview.copy_(codes.view(-1).cuda())
     scales = torch.full((96, 2), 120, dtype=torch.uint8, device="cuda")
     buf, view = guarded(96 * 64 * 2)
     y = view.view(torch.bfloat16).view(96, 64)
-    mx.mx_dequantize(codes, scales, "e4m3", (96, 64), "bf16", out=y)
+    mx.mx_dequantize(cview.view(96, nbytes), scales, fmt, (96, 64), "bf16", out=y)
     torch.cuda.synchronize()
     b = buf.cpu().numpy()
     assert (b[:GUARD] == CANARY).all() and (b[-GUARD:] == CANARY).all()
+    ref = O.dequantize(codes.numpy(), scales.cpu().numpy(), OFMT[fmt], "bf16")
+    assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), ref)
 
 
 def test_runs_on_the_callers_stream(mx):

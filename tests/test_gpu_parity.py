@@ -12,10 +12,11 @@ import oracle as O
 
 pytestmark = pytest.mark.gpu
 
-OFMT = {"e4m3": O.E4M3, "e5m2": O.E5M2, "e2m1": O.E2M1}
+OFMT = {"e4m3": O.E4M3, "e5m2": O.E5M2, "e2m1": O.E2M1, "e2m3": O.E2M3, "e3m2": O.E3M2, "int8": O.INT8}
 OMODE = {"floor": O.FLOOR, "roundup": O.ROUNDUP}
 OAXIS = {"row": O.ROW, "col": O.COL, "both": O.BOTH}
-FMTS = ["e4m3", "e5m2", "e2m1"]
+FMTS = ["e4m3", "e5m2", "e2m1", "e2m3", "e3m2", "int8"]
+NEW_FMTS = ["e2m3", "e3m2", "int8"]          # the MXFP6 and MXINT8 rows of the family table
 MODES = ["floor", "roundup"]
 
 
@@ -159,6 +160,38 @@ def test_ragged_shapes(mx, fmt, dt):
             check(mx, x, fmt, mode, axis, f"ragged {(b, r, c, axis, mode)}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt", NEW_FMTS)
+def test_new_formats_workloads(mx, fmt, mode):
+    """MXFP6 / MXINT8 on the workload tensors at small sizes: BF16 activations
+    fused (several tiles, ragged tails), BF16 weights row-wise, FP32 gradients
+    with specials column-wise and fused."""
+    for shape in ((544, 416), (96, 4128), (32, 32)):
+        check(mx, I.activations(*shape, seed=31), fmt, mode, "both", f"act{shape}")
+    check(mx, I.weights(352, 288, seed=32), fmt, mode, "row", "weights")
+    g = I.gradients(288, 352, seed=33)
+    check(mx, g, fmt, mode, "col", "grads/col")
+    check(mx, g, fmt, mode, "both", "grads/both")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", NEW_FMTS)
+def test_new_formats_round_trip(mx, fmt, out_dtype):
+    b, r, c = 2, 160, 288
+    x = torch.stack([I.wide_range(i, r, c, seed=34) for i in range(b)])
+    got = gpu_quant(mx, x, fmt, "floor", "both")
+    exp = oracle_quant(x, fmt, "floor", "both")
+    assert_same(got, exp, "wide")
+    for plane, shp in (("row", (b, r, c)), ("col", (b, c, r))):
+        y = mx.mx_dequantize(torch.from_numpy(got[f"{plane}_codes"]).cuda(),
+                             torch.from_numpy(got[f"{plane}_scales"]).cuda(), fmt, shp, out_dtype)
+        torch.cuda.synchronize()
+        ref = O.dequantize(exp[f"{plane}_codes"], exp[f"{plane}_scales"], OFMT[fmt], out_dtype)
+        yb = y.cpu().contiguous()
+        yb = yb.view(torch.int16).numpy().view(np.uint16) if out_dtype == "bf16" else yb.numpy().view(np.uint32)
+        assert np.array_equal(yb, ref), plane
+
+
 # ---------------- dequantization ----------------
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
@@ -170,7 +203,7 @@ def test_dequant_every_code_and_scale(mx, fmt, out_dtype):
     scales = np.repeat(np.arange(256, dtype=np.uint8), ncode)
     blocks = np.zeros((codes.size, 32), dtype=np.uint8)
     blocks[:, :] = codes[:, None]                         # whole block holds the code
-    packed = O.pack_e2m1(blocks) if fmt == "e2m1" else blocks
+    packed = O.pack_codes(blocks, OFMT[fmt])
     sc = scales.reshape(-1, 1)
     y = mx.mx_dequantize(torch.from_numpy(np.ascontiguousarray(packed)).cuda(), torch.from_numpy(sc).cuda(),
                          fmt, (blocks.shape[0], 32), out_dtype)
@@ -188,7 +221,7 @@ def slab_check(mx_out, x_slab_cpu, r0, fmt, mode, axis, batch_index=None):
     """Compare the rows r0..r0+n of the GPU planes with the oracle on that slab."""
     n = x_slab_cpu.shape[0]
     exp = oracle_quant(x_slab_cpu, fmt, mode, axis)
-    div = 2 if fmt == "e2m1" else 1
+    bits = OFMT[fmt].bits
     for k, e in exp.items():
         t = mx_out[k] if batch_index is None else mx_out[k][batch_index]
         if k == "row_codes":
@@ -196,7 +229,7 @@ def slab_check(mx_out, x_slab_cpu, r0, fmt, mode, axis, batch_index=None):
         elif k == "row_scales":
             g = t[r0:r0 + n]
         elif k == "col_codes":
-            g = t[:, r0 // div:(r0 + n) // div]
+            g = t[:, r0 * bits // 8:(r0 + n) * bits // 8]
         else:
             g = t[:, r0 // 32:(r0 + n) // 32]
         g = g.cpu().numpy()
@@ -220,6 +253,29 @@ def test_full_weights_e2m1(mx, mode):
     torch.cuda.synchronize()
     for r0 in (0, 7000, 14336 - 256):
         slab_check(out, x[r0:r0 + 256].cpu(), r0, "e2m1", mode, "row")
+
+
+@pytest.mark.parametrize("fmt", NEW_FMTS)
+def test_full_activations_new_formats(mx, fmt):
+    """16384x4096 BF16 activations, fused row+column MXFP6 / MXINT8, sampled slabs."""
+    x = I.activations(16384, 4096, seed=1, device="cuda")
+    out = mx.mx_quantize(x, fmt, "floor", "both")
+    torch.cuda.synchronize()
+    for r0 in (0, 8192 - 128, 16384 - 256):
+        slab_check(out, x[r0:r0 + 256].cpu(), r0, fmt, "floor", "both")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m3"])
+def test_tall_column_plane_addressing(mx, fmt):
+    """4194432 x 256 BF16 (column-plane rows above 2^22 bytes apart): the slab
+    that crosses row 2^22, every one of the 256 columns."""
+    R, C = (1 << 22) + 128, 256
+    x = I.activations(R, C, seed=35, device="cuda")
+    out = mx.mx_quantize(x, fmt, "floor", "both")
+    torch.cuda.synchronize()
+    for r0 in ((1 << 22) - 128, R - 256):
+        slab_check(out, x[r0:r0 + 256].cpu(), r0, fmt, "floor", "both")
+    del out, x
 
 
 def test_full_gradients_e5m2_col(mx):
