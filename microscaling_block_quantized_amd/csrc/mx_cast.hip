@@ -20,10 +20,12 @@
 //   * column blocks: in-lane max over the thread's RPT rows, then a max over
 //     the RG lanes holding the other rows of the block. The codes (1 byte, not
 //     the inputs) are staged in LDS as [column][row] with a 16-byte XOR swizzle
-//     and written out as 128-byte runs of the transposed plane.
+//     and written out as runs of the transposed plane (128 bytes per column
+//     for 8-bit codes; 6-bit codes are packed 16 -> 12 bytes on the way out).
 // Memory-system choices, measured on MI355X with input and output buffers
 // rotated through more memory than the 256 MB last-level cache holds: the
-// input is read and both code planes are written with non-temporal accesses,
+// input is read and both code planes are written with non-temporal accesses
+// (6-bit code planes excepted: their runs do not fill whole 128-byte lines),
 // while the scale planes go through L2 with ordinary stores (scale bytes of one
 // 128-byte line come from several workgroups and must merge in L2; making them
 // non-temporal costs 60%). Tiles are ordered so that each XCD owns a strip of
@@ -64,6 +66,17 @@ __device__ __forceinline__ void store_nt12(void* p, uint32_t a, uint32_t b, uint
   __builtin_nontemporal_store(a, q);
   __builtin_nontemporal_store(b, q + 1);
   __builtin_nontemporal_store(c, q + 2);
+}
+// The same through L2 with ordinary stores. A tile's 6-bit code runs are 96 or
+// 192 bytes long, so 128-byte lines are shared by neighbouring tiles (which the
+// tile order keeps on one XCD at about the same time); ordinary stores let
+// those partial lines merge in L2 before they are written back. Non-temporal
+// partial lines made the fused FP6 cast 36% slower on MI355X.
+__device__ __forceinline__ void store12(void* p, uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+  q[0] = a;
+  q[1] = b;
+  q[2] = c;
 }
 __device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
   __builtin_nontemporal_store(static_cast<unsigned short>(v), reinterpret_cast<unsigned short*>(p));
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
           const uint32_t hi = pack6(w.y);
           const uint32_t e0 = pack6(w.x) | (hi << 24), e1 = hi >> 8;
           const uint32_t o0 = dpp<kDppXor1>(e0), o1 = dpp<kDppXor1>(e1);
-          if (ok && (t & 1) == 0) store_nt12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+          if (ok && (t & 1) == 0) store12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
         } else if (ok) {
           if constexpr (CB == 8) store_nt8(dst, w);
           else store_nt4(dst, w.x);
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
           // 24 bits per lane: lane 4i stores the 12 bytes of lanes 4i .. 4i+3
           const uint32_t g0 = pack6(w);
           const uint32_t g1 = dpp<kDppQuadNext>(g0), g2 = dpp<kDppXor2>(g0), g3 = dpp<kDppQuadPrev>(g0);
-          if (ok && (t & 3) == 0) store_nt12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+          if (ok && (t & 3) == 0) store12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
         } else if (ok) {
           if constexpr (CB == 8) store_nt4(dst, w);
           else store_nt2(dst, w);
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         uint8_t* dst = cct + uint32_t(cl) * cpitch + uint32_t(part) * OUT_CHUNK;
         if constexpr (CB == 6) {
           const uint3 p = pack6x16(w.x, w.y, w.z, w.w);
-          store_nt12(dst, p.x, p.y, p.z);
+          store12(dst, p.x, p.y, p.z);
         } else {
           store_nt16(dst, w);
         }
