@@ -6,4 +6,8 @@ Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from the library.
 """
 from .mx_oracle import *  # noqa: F401,F403
-from .mx_oracle import __all__  # noqa: F401
+from .mx_oracle import __all__ as _base_all
+from .mx_variants import *  # noqa: F401,F403
+from .mx_variants import __all__ as _variant_all
+
+__all__ = list(_base_all) + list(_variant_all)

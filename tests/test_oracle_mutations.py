@@ -204,3 +204,82 @@ def test_pins_catch_int8_sign_magnitude():
 def test_pins_catch_e3m2_bias():
     with planted("decode_code", decode_e3m2_bias_4):
         assert any_pin_fails([(P6.test_fp6_tables_are_fp8_low_binades, ("e3m2",))])
+
+
+# ---- stochastic rounding, random bits, 2-D blocks ----
+
+import oracle.mx_variants as V  # noqa: E402
+import test_oracle_variants as PV  # noqa: E402
+
+
+@contextlib.contextmanager
+def planted_v(name, fn):
+    old = getattr(V, name)
+    setattr(V, name, fn)
+    setattr(O, name, fn)
+    try:
+        yield
+    finally:
+        setattr(V, name, old)
+        setattr(O, name, old)
+
+
+def test_pins_catch_philox_swapped_multipliers():
+    orig = V.philox4x32_10
+
+    def swapped(ctr, key):
+        V._M0, V._M1 = V._M1, V._M0
+        try:
+            return orig(ctr, key)
+        finally:
+            V._M0, V._M1 = V._M1, V._M0
+    with planted_v("philox4x32_10", swapped):
+        assert any_pin_fails([(PV.test_philox_known_answers, KAT) for KAT in PV.KAT])
+
+
+def test_pins_catch_sr_ge_comparison():
+    def ge(s, fmt, u16):
+        """f >= u instead of f > u: a draw of 0 then moves grid values up."""
+        s = np.asarray(s, dtype=np.float64)
+        a = np.abs(s)
+        nz = a > 0
+        q = V._spacing(np.where(nz, a, 1.0), fmt)
+        x = a / q
+        n = np.floor(x)
+        up = (x - n) >= np.asarray(u16, dtype=np.float64) / 65536.0
+        mag = np.where(a >= M.max_finite(fmt), M.max_finite(fmt), (n + up) * q)
+        return M.encode_elements(np.copysign(np.where(nz, mag, 0.0), s), fmt)
+    with planted_v("encode_elements_sr", ge):
+        assert any_pin_fails([(PV.test_sr_leaves_grid_values_and_saturates, ()),
+                              (PV.test_sr_up_count_over_all_draws, (O.E2M1,))])
+
+
+def test_pins_catch_sr_bits_in_transposed_order():
+    orig = V.quantize_ex
+
+    def transposed_bits(x, in_dtype, fmt, mode, axis, rounding="rne", seed=0, block="1x32"):
+        if rounding != "sr" or not (axis & O.COL):
+            return orig(x, in_dtype, fmt, mode, axis, rounding, seed, block)
+        # column copy drawn with X^T's own flat order
+        xt = np.ascontiguousarray(np.swapaxes(np.asarray(x), -1, -2))
+        out = orig(x, in_dtype, fmt, mode, axis & O.ROW, rounding, seed, block) if axis & O.ROW else {}
+        t = orig(xt, in_dtype, fmt, mode, O.ROW, rounding, seed, block)
+        out["col_codes"], out["col_scales"] = t["row_codes"], t["row_scales"]
+        return out
+    with planted_v("quantize_ex", transposed_bits):
+        assert any_pin_fails([(PV.test_sr_column_copy_uses_the_elements_bits, ())])
+
+
+def test_pins_catch_2d_scale_from_first_row():
+    orig_plane = V._quant_plane
+
+    def plane(x64, u, fmt, mode, block):
+        """Each 32x32 tile takes the scale of its first row only."""
+        if block != "32x32":
+            return orig_plane(x64, u, fmt, mode, block)
+        first = np.repeat(x64[:, ::32, :], 32, axis=1)
+        _, scales_f = orig_plane(first, u, fmt, mode, block)
+        codes, _ = orig_plane(x64, u, fmt, mode, block)
+        return codes, scales_f
+    with planted_v("_quant_plane", plane):
+        assert any_pin_fails([(PV.test_2d_scale_is_max_of_row_block_scales, (O.E4M3, O.FLOOR))])
