@@ -34,6 +34,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "GB/s (read+write) and % of HBM peak, MXFP8 row+col cast 16384×4096"
 COUNTERS = os.path.join(ROOT, "profiles", "fused_cast_e4m3_16384x4096_counters.txt")
 KERNEL_SOURCES = ["microscaling_block_quantized_amd/csrc/mx_cast.hip",
+                  "microscaling_block_quantized_amd/csrc/mx_cast_impl.h",
+                  "microscaling_block_quantized_amd/csrc/mx_sr.h",
                   "microscaling_block_quantized_amd/csrc/mx_device.h"]
 
 
@@ -72,7 +74,7 @@ def copy_bytes(alg_bytes: int) -> int:
 
 
 COPY_BYTES = copy_bytes(ALG_BYTES)   # each ceiling copy of the fused workload reads and writes this much
-CAST_KERNEL = "mx_cast_kernel<true, 0, 0, 3>"
+CAST_KERNEL = "mx_cast_kernel<true, 0, 0, 3, 0, false>"
 
 
 def _csv_rows(path):
@@ -161,31 +163,37 @@ def cpu_baseline(x_gpu, budget_s: float = 12.0):
 CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "int8": 8}
 
 
-def _planes(dev, b, r, c, fmt, axis):
+def _planes(dev, b, r, c, fmt, axis, block="1x32"):
     import torch
     bits = CODE_BITS[fmt]
+    two = block == "32x32"
     out = {}
     if axis in ("row", "both"):
         out["row_codes"] = torch.empty((b, r, c * bits // 8), dtype=torch.uint8, device=dev)
-        out["row_scales"] = torch.empty((b, r, c // 32), dtype=torch.uint8, device=dev)
+        out["row_scales"] = torch.empty((b, r // 32, c // 32) if two else (b, r, c // 32), dtype=torch.uint8,
+                                        device=dev)
     if axis in ("col", "both"):
         out["col_codes"] = torch.empty((b, c, r * bits // 8), dtype=torch.uint8, device=dev)
-        out["col_scales"] = torch.empty((b, c, r // 32), dtype=torch.uint8, device=dev)
+        out["col_scales"] = torch.empty((b, c // 32, r // 32) if two else (b, c, r // 32), dtype=torch.uint8,
+                                        device=dev)
     return out
 
 
-def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc):
+def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc, rounding="rne", block="1x32"):
     """One quantize launch per step over one tensor; bytes = input + code and scale planes."""
     planes = (2 if axis == "both" else 1)
-    nbytes = b * r * c * esize + planes * (b * r * c * CODE_BITS[fmt] // 8 + b * r * c // 32)
+    per_scale = 32 * 32 if block == "32x32" else 32
+    nbytes = b * r * c * esize + planes * (b * r * c * CODE_BITS[fmt] // 8 + b * r * c // per_scale)
 
     def make(dev, i):
         import microscaling_block_quantized_amd as mx
         x = gen(dev, i).reshape(b, r, c)
-        return mx.BoundQuantize(x, fmt, mode, axis, _planes(dev, b, r, c, fmt, axis))
-    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
-            "config": {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": fmt, "scale_mode": mode,
-                       "axis": axis}}
+        return mx.BoundQuantize(x, fmt, mode, axis, _planes(dev, b, r, c, fmt, axis, block), rounding=rounding,
+                                seed=0x5EED + i, block=block)
+    cfg = {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": fmt, "scale_mode": mode, "axis": axis}
+    if rounding != "rne" or block != "1x32":
+        cfg.update(rounding=rounding, block=block)
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "config": cfg}
 
 
 def _wide_range_pipeline():
@@ -272,6 +280,12 @@ WORKLOADS = {
                                "activations 16384x4096 bf16 -> MXFP6 E3M2 row+col fused, floor scale rule"),
     "act_int8": _cast_workload(_gen("activations"), 1, ROWS, COLS, 2, "int8", "floor", "both",
                                "activations 16384x4096 bf16 -> MXINT8 row+col fused, floor scale rule"),
+    "grad_sr_e2m1": _cast_workload(_gen("gradients"), 1, 8192, 8192, 4, "e2m1", "roundup", "col",
+                                   "gradients 8192x8192 fp32 -> MXFP4 E2M1 column-wise, stochastic rounding, "
+                                   "round-up scale rule", rounding="sr"),
+    "weights_2d_e2m1": _cast_workload(_gen("weights"), 1, 14336, 4096, 2, "e2m1", "floor", "both",
+                                      "weights 14336x4096 bf16 -> MXFP4 E2M1 32x32 blocks, row+col fused, "
+                                      "floor scale rule", block="32x32"),
     "wide_range": _wide_range_pipeline(),
     "fp32_normal": _fp32_normal_round_trip(),
 }

@@ -73,6 +73,34 @@ typedef struct {
   int64_t batch, rows, cols;
 } mx_shape;
 
+/* Rounding of the elements (same article: §2 requires round-to-nearest-even for
+ * the FP4 conversion; §4's 4-bit pretraining recipe rounds gradients
+ * stochastically, and §11 lists stochastic rounding among the P3109 modes).
+ * MX_ROUND_STOCHASTIC: a scaled value s with |s| < max goes to the grid value
+ *   above |s| when the fraction f of |s| between its two neighbouring grid
+ *   values exceeds u / 2^16, else to the one below; |s| >= max saturates; the
+ *   sign is kept. u is 16 bits of Philox4x32-10 (Salmon et al., SC'11) keyed
+ *   by the 64-bit seed (key word 0 = low half): element i of X's flat
+ *   [batch][rows][cols] order uses the output block of counter
+ *   (i >> 3, 0, 0) (the 64-bit i >> 3 in words 0-1), its word (i >> 1) & 3,
+ *   low half for even i, high half for odd i. The row and column copies of an
+ *   element use the same u. Scales are chosen as for nearest-even. */
+typedef enum { MX_ROUND_NEAREST_EVEN = 0, MX_ROUND_STOCHASTIC = 1 } mx_rounding;
+
+/* Block shape (same article §4: the recipe scales weights in two-dimensional
+ * blocks). MX_BLOCK_32X32: one E8M0 scale per 32x32 tile of each batch slice,
+ * chosen from the tile's largest magnitude by the same rules; the row copy's
+ * scale plane is [batch][rows/32][cols/32] and the column copy (the same cast
+ * of X^T) has codes [batch][cols][rows'] and scales [batch][cols/32][rows/32].
+ * rows and cols must both be multiples of 32. */
+typedef enum { MX_BLOCK_1X32 = 0, MX_BLOCK_32X32 = 1 } mx_block;
+
+typedef struct {
+  mx_rounding rounding;
+  mx_block block;
+  uint64_t seed;        /* used by MX_ROUND_STOCHASTIC only */
+} mx_quant_opts;
+
 #define MX_OK 0
 #define MX_ERR_NULL (-1)        /* a required pointer is NULL, or an unused one is not */
 #define MX_ERR_SHAPE (-2)       /* non-positive extent, or a blocked extent % 32 != 0 */
@@ -116,6 +144,23 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
  * aligned (E2M1 8-byte, E2M3/E3M2 4-byte). y must not overlap codes or scales. */
 int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s,
                   mx_dtype y_dtype, void* y, void* stream);
+
+/* mx_quantize with options; opts == NULL means nearest-even and 1x32 blocks,
+ * which is exactly mx_quantize. With MX_BLOCK_32X32 the scale planes hold
+ * batch*rows*cols/1024 bytes each (layout above) and rows % 32 == 0 also for
+ * MX_AXIS_ROW; the code planes are as for mx_quantize. Errors as mx_quantize,
+ * plus MX_ERR_ENUM for an unknown rounding or block. The result depends only on
+ * the inputs, the options and the seed (not on the launch or the device). */
+int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
+                   mx_axis axis, const mx_quant_opts* opts, void* row_codes, uint8_t* row_scales,
+                   void* col_codes, uint8_t* col_scales, void* stream);
+
+/* mx_dequantize for either block shape. With MX_BLOCK_32X32, scales is the
+ * [batch][rows/32][cols/32] grid of the plane as stored (a column plane passes
+ * [batch][cols][rows] with its [batch][cols/32][rows/32] grid) and rows % 32
+ * must be 0. MX_BLOCK_1X32 is exactly mx_dequantize. */
+int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s, mx_block block,
+                     mx_dtype y_dtype, void* y, void* stream);
 
 /* Static text for an MX_* code; never NULL. */
 const char* mx_strerror(int err);

@@ -4,8 +4,11 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libmx.so``. torch provides device memory and the current stream.
 The functions mirror the C ABI in ``include/libmx.h``:
 
-    mx_quantize(x, fmt, mode, axis)      -> dict of uint8 code / scale planes
-    mx_dequantize(codes, scales, fmt, shape, out_dtype)
+    mx_quantize(x, fmt, mode, axis, rounding, seed, block)
+                                         -> dict of uint8 code / scale planes
+                                            (mx_quantize_ex when rounding or block
+                                            is not the default)
+    mx_dequantize(codes, scales, fmt, shape, out_dtype, block)
     mx_plane_bytes(fmt, shape)           -> (code bytes, scale bytes) of one plane
     mx_strerror(err), mx_version()
 
@@ -18,7 +21,7 @@ import ctypes
 import os
 
 __all__ = [
-    "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "lib_path", "load", "mx_version", "mx_strerror",
+    "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "ROUNDING", "BLOCK", "MxQuantOpts", "lib_path", "load", "mx_version", "mx_strerror",
     "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize", "BoundDequantize",
 ]
 
@@ -26,8 +29,11 @@ FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4, "int8": 5}
 CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "int8": 8}
 MODE = {"floor": 0, "roundup": 1}
 AXIS = {"row": 1, "col": 2, "both": 3}
+ROUNDING = {"rne": 0, "sr": 1}
+BLOCK = {"1x32": 0, "32x32": 1}
 DTYPE = {"f32": 0, "bf16": 1}
-EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_strerror", "mx_version")
+EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_quantize_ex", "mx_dequantize", "mx_dequantize_ex",
+           "mx_strerror", "mx_version")
 
 _LIB = None
 
@@ -40,6 +46,10 @@ class MXError(RuntimeError):
 
 class MxShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class MxQuantOpts(ctypes.Structure):
+    _fields_ = [("rounding", ctypes.c_int), ("block", ctypes.c_int), ("seed", ctypes.c_uint64)]
 
 
 def lib_path() -> str:
@@ -68,6 +78,11 @@ def load() -> ctypes.CDLL:
     lib.mx_quantize.argtypes = [vp, i32, MxShape, i32, i32, i32, vp, u8p, vp, u8p, vp]
     lib.mx_dequantize.restype = i32
     lib.mx_dequantize.argtypes = [vp, u8p, i32, MxShape, i32, vp, vp]
+    lib.mx_quantize_ex.restype = i32
+    lib.mx_quantize_ex.argtypes = [vp, i32, MxShape, i32, i32, i32, ctypes.POINTER(MxQuantOpts), vp, u8p, vp,
+                                   u8p, vp]
+    lib.mx_dequantize_ex.restype = i32
+    lib.mx_dequantize_ex.argtypes = [vp, u8p, i32, MxShape, i32, i32, vp, vp]
     _LIB = lib
     return lib
 
@@ -107,14 +122,23 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
 
 
-def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", out: dict | None = None):
+def _opts(rounding: str, seed: int, block: str):
+    if rounding == "rne" and block == "1x32":
+        return None
+    return MxQuantOpts(ROUNDING[rounding], BLOCK[block], int(seed) & ((1 << 64) - 1))
+
+
+def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", out: dict | None = None,
+                rounding: str = "rne", seed: int = 0, block: str = "1x32"):
     """Quantize a GPU tensor [R][C] or [B][R][C] (bfloat16 or float32).
 
     Returns {"row_codes", "row_scales"} and/or {"col_codes", "col_scales"} as
     uint8 tensors: row planes [B][R][C'] / [B][R][C/32], column planes
     [B][C][R'] / [B][C][R/32] (C' = C * code bits / 8: C for the 8-bit
     formats, 3C/4 for e2m3 / e3m2, C/2 for e2m1); the batch axis is dropped
-    for a 2-D input. ``out`` may supply preallocated planes.
+    for a 2-D input. ``out`` may supply preallocated planes. rounding "sr"
+    (stochastic, with ``seed``) and block "32x32" (scales [B][R/32][C/32] and
+    [B][C/32][R/32]) go through mx_quantize_ex.
     """
     import torch
     if not x.is_cuda:
@@ -134,28 +158,35 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
         t = out.get(name)
         return t if t is not None else torch.empty(shp, dtype=torch.uint8, device=dev)
 
+    opts = _opts(rounding, seed, block)
+    b2 = block == "32x32"
     planes = {}
     if ax & 1:
         planes["row_codes"] = plane("row_codes", (b, r, c * bits // 8))
-        planes["row_scales"] = plane("row_scales", (b, r, c // 32))
+        planes["row_scales"] = plane("row_scales", (b, max(r // 32, 1), c // 32) if b2 else (b, r, c // 32))
     if ax & 2:
         planes["col_codes"] = plane("col_codes", (b, c, r * bits // 8))
-        planes["col_scales"] = plane("col_scales", (b, c, max(r // 32, 1)))
+        planes["col_scales"] = plane("col_scales", (b, c // 32, max(r // 32, 1)) if b2 else (b, c, max(r // 32, 1)))
+    args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
+            MODE[mode], ax)
+    outs = (_ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")), _ptr(planes.get("col_codes")),
+            _ptr(planes.get("col_scales")), _stream_of(x))
     with torch.cuda.device(dev):
-        err = load().mx_quantize(
-            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
-            MODE[mode], ax, _ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")),
-            _ptr(planes.get("col_codes")), _ptr(planes.get("col_scales")), _stream_of(x))
+        if opts is None:
+            err = load().mx_quantize(*args, *outs)
+        else:
+            err = load().mx_quantize_ex(*args, ctypes.byref(opts), *outs)
     if err:
-        raise MXError(err, "mx_quantize")
+        raise MXError(err, "mx_quantize_ex" if opts is not None else "mx_quantize")
     if squeeze:
         planes = {k: v[0] for k, v in planes.items()}
     return planes
 
 
-def mx_dequantize(codes, scales, fmt: str, shape, out_dtype: str = "f32", out=None):
+def mx_dequantize(codes, scales, fmt: str, shape, out_dtype: str = "f32", out=None, block: str = "1x32"):
     """Dequantize one plane; ``shape`` is the element shape of the plane as stored
-    (blocks of 32 along its last axis). Returns a float32 or bfloat16 GPU tensor."""
+    (blocks of 32 along its last axis, or 32x32 tiles with block "32x32").
+    Returns a float32 or bfloat16 GPU tensor."""
     import torch
     if not codes.is_cuda or not scales.is_cuda:
         raise ValueError("mx_dequantize needs GPU tensors (libmx has no CPU path)")
@@ -167,8 +198,12 @@ def mx_dequantize(codes, scales, fmt: str, shape, out_dtype: str = "f32", out=No
     tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=codes.device)
     with torch.cuda.device(codes.device):
-        err = load().mx_dequantize(_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c), DTYPE[out_dtype],
-                                   _ptr(y), _stream_of(codes))
+        if block == "1x32":
+            err = load().mx_dequantize(_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c), DTYPE[out_dtype],
+                                       _ptr(y), _stream_of(codes))
+        else:
+            err = load().mx_dequantize_ex(_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c), BLOCK[block],
+                                          DTYPE[out_dtype], _ptr(y), _stream_of(codes))
     if err:
         raise MXError(err, "mx_dequantize")
     return y
@@ -179,14 +214,21 @@ class BoundQuantize:
     launches over fixed buffers (benchmark loops). Calling it enqueues one
     quantize on the stream that was current at construction."""
 
-    def __init__(self, x, fmt: str, mode: str, axis: str, out: dict):
+    def __init__(self, x, fmt: str, mode: str, axis: str, out: dict, rounding: str = "rne", seed: int = 0,
+                 block: str = "1x32"):
         import torch
         b, r, c = _shape3(x.shape)
-        self._fn = load().mx_quantize
-        self._args = (
-            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
-            MODE[mode], AXIS[axis], _ptr(out.get("row_codes")), _ptr(out.get("row_scales")),
-            _ptr(out.get("col_codes")), _ptr(out.get("col_scales")), _stream_of(x))
+        head = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
+                MODE[mode], AXIS[axis])
+        tail = (_ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
+                _ptr(out.get("col_scales")), _stream_of(x))
+        self._opts = _opts(rounding, seed, block)
+        if self._opts is None:
+            self._fn = load().mx_quantize
+            self._args = head + tail
+        else:
+            self._fn = load().mx_quantize_ex
+            self._args = head + (ctypes.byref(self._opts),) + tail
         self._keep = (x, out)
 
     def __call__(self) -> None:

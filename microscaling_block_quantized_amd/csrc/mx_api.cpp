@@ -19,6 +19,8 @@ bool valid_fmt(int f) {
 bool valid_mode(int m) { return m == MX_SCALE_FLOOR || m == MX_SCALE_ROUNDUP; }
 bool valid_dtype(int d) { return d == MX_F32 || d == MX_BF16; }
 bool valid_axis(int a) { return a == MX_AXIS_ROW || a == MX_AXIS_COL || a == MX_AXIS_BOTH; }
+bool valid_rounding(int r) { return r == MX_ROUND_NEAREST_EVEN || r == MX_ROUND_STOCHASTIC; }
+bool valid_block(int b) { return b == MX_BLOCK_1X32 || b == MX_BLOCK_32X32; }
 
 int code_bits(int fmt) { return fmt == MX_E2M1 ? 4 : (fmt == MX_E2M3 || fmt == MX_E3M2) ? 6 : 8; }
 // dequantize reads 16 codes per thread: 16, 12 or 8 bytes
@@ -53,7 +55,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10100; }
+int mx_version(void) { return 10200; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -82,8 +84,19 @@ int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_byt
 int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
                 mx_axis axis, void* row_codes, uint8_t* row_scales, void* col_codes,
                 uint8_t* col_scales, void* stream) {
-  if (!valid_fmt(fmt) || !valid_mode(mode) || !valid_dtype(x_dtype) || !valid_axis(axis))
+  return mx_quantize_ex(x, x_dtype, s, fmt, mode, axis, nullptr, row_codes, row_scales, col_codes, col_scales,
+                        stream);
+}
+
+int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
+                   mx_axis axis, const mx_quant_opts* opts, void* row_codes, uint8_t* row_scales,
+                   void* col_codes, uint8_t* col_scales, void* stream) {
+  const mx_quant_opts o = opts ? *opts : mx_quant_opts{MX_ROUND_NEAREST_EVEN, MX_BLOCK_1X32, 0};
+  if (!valid_fmt(fmt) || !valid_mode(mode) || !valid_dtype(x_dtype) || !valid_axis(axis) ||
+      !valid_rounding(o.rounding) || !valid_block(o.block))
     return MX_ERR_ENUM;
+  const bool b2d = o.block == MX_BLOCK_32X32;
+  const bool sr = o.rounding == MX_ROUND_STOCHASTIC;
   const bool want_row = (axis & MX_AXIS_ROW) != 0;
   const bool want_col = (axis & MX_AXIS_COL) != 0;
   if (x == nullptr) return MX_ERR_NULL;
@@ -91,13 +104,13 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
   if (want_col != (col_codes != nullptr) || want_col != (col_scales != nullptr)) return MX_ERR_NULL;
   const int64_t n = elements(s);
   if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
-  if (want_col && s.rows % kBlock != 0) return MX_ERR_SHAPE;
+  if ((want_col || b2d) && s.rows % kBlock != 0) return MX_ERR_SHAPE;
   if (!aligned(x, 16) || (want_row && !aligned(row_codes, 16)) || (want_col && !aligned(col_codes, 16)))
     return MX_ERR_ALIGN;
 
   const int64_t in_bytes = n * (x_dtype == MX_BF16 ? 2 : 4);
   const int64_t cbytes = n / 8 * code_bits(fmt);
-  const int64_t sbytes = n / kBlock;
+  const int64_t sbytes = n / (b2d ? kBlock * kBlock : kBlock);
   Range rs[5];
   int nr = 0;
   rs[nr++] = range_of(x, in_bytes);
@@ -107,7 +120,8 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
     for (int j = i + 1; j < nr; ++j)
       if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
 
-  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, int(axis));
+  const bool row_stream = axis == MX_AXIS_ROW && !b2d;
+  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, row_stream);
   if (g.blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
   // per-thread offsets inside a tile are 32-bit: 128 rows of FP32 and 256 column-plane rows
   if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;
@@ -124,30 +138,43 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
   a.tiles_r = uint32_t(g.tiles_r);
   a.tiles_c = uint32_t(g.tiles_c);
   a.flags = 0;
+  a.seed_lo = uint32_t(o.seed);
+  a.seed_hi = uint32_t(o.seed >> 32);
   // the row-only kernel stores 4 scale bytes of consecutive blocks at once (any cols);
-  // the tiled kernel stores the 4 of one row's 128 columns (cols % 128 == 0)
-  if (want_row && aligned(row_scales, 4) && (axis == MX_AXIS_ROW || s.cols % 128 == 0))
-    a.flags |= mx::kRowScaleDword;
+  // the tiled kernel stores the 4 of one row's 128 columns (cols % 128 == 0) or, with
+  // 32x32 blocks, of 128 columns in one row of the scale grid (same condition)
+  if (want_row && aligned(row_scales, 4) && (row_stream || s.cols % 128 == 0)) a.flags |= mx::kRowScaleDword;
   if (want_col && s.rows % 128 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
-  const hipError_t e = mx::launch_cast(x_dtype == MX_BF16, int(fmt), int(mode), int(axis), a,
-                                       uint32_t(g.blocks), static_cast<hipStream_t>(stream));
+  const bool bf = x_dtype == MX_BF16;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint32_t nb = uint32_t(g.blocks);
+  hipError_t e;
+  if (sr) e = mx::launch_cast_sr(bf, int(fmt), int(mode), int(axis), b2d, a, nb, st);
+  else if (b2d) e = mx::launch_cast_2d(bf, int(fmt), int(mode), int(axis), a, nb, st);
+  else e = mx::launch_cast(bf, int(fmt), int(mode), int(axis), a, nb, st);
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
 int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s,
                   mx_dtype y_dtype, void* y, void* stream) {
-  if (!valid_fmt(fmt) || !valid_dtype(y_dtype)) return MX_ERR_ENUM;
+  return mx_dequantize_ex(codes, scales, fmt, s, MX_BLOCK_1X32, y_dtype, y, stream);
+}
+
+int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s, mx_block block,
+                     mx_dtype y_dtype, void* y, void* stream) {
+  if (!valid_fmt(fmt) || !valid_dtype(y_dtype) || !valid_block(block)) return MX_ERR_ENUM;
   if (codes == nullptr || scales == nullptr || y == nullptr) return MX_ERR_NULL;
+  const bool b2d = block == MX_BLOCK_32X32;
   const int64_t n = elements(s);
-  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
+  if (n < 0 || s.cols % kBlock != 0 || (b2d && s.rows % kBlock != 0)) return MX_ERR_SHAPE;
   if (!aligned(codes, dequant_code_align(fmt)) || !aligned(y, 16)) return MX_ERR_ALIGN;
   const Range rc = range_of(codes, n / 8 * code_bits(fmt));
-  const Range rsc = range_of(scales, n / kBlock);
+  const Range rsc = range_of(scales, n / (b2d ? kBlock * kBlock : kBlock));
   const Range ry = range_of(y, n * (y_dtype == MX_BF16 ? 2 : 4));
   if (overlap(ry, rc) || overlap(ry, rsc)) return MX_ERR_ALIAS;
   if ((n / 16 + 255) / 256 > kMaxGrid) return MX_ERR_TOO_LARGE;
   const hipError_t e = mx::launch_dequant(int(fmt), y_dtype == MX_BF16, static_cast<const uint8_t*>(codes),
-                                          scales, y, n, static_cast<hipStream_t>(stream));
+                                          scales, y, n, b2d ? s.cols : 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 

@@ -96,13 +96,21 @@ __device__ __forceinline__ void decode16(const uint32_t* cw, uint32_t k, float* 
   }
 }
 
-template <int F, bool OUT_BF16>
+// B2: 32x32 blocks over rows of `cols` elements; the scale of chunk i (row
+// r = 16 i / cols, column c = 16 i % cols) is scales[(r / 32) * (cols / 32) + c / 32].
+template <int F, bool OUT_BF16, bool B2>
 __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
-                                                             void* __restrict__ y, int64_t nchunks) {
+                                                             void* __restrict__ y, int64_t nchunks, int64_t cols) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;   // 16-element chunk
   if (i >= nchunks) return;
-  const uint32_t k = scales[i >> 1];
+  int64_t si = i >> 1;
+  if constexpr (B2) {
+    const int64_t cpr = cols / 16;                                    // chunks per row
+    const int64_t r = i / cpr, c = i - r * cpr;
+    si = (r >> 5) * (cols >> 5) + (c >> 1);
+  }
+  const uint32_t k = scales[si];
   uint32_t cw[4];
   if constexpr (F == kE2M1) {
     const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(codes + i * 8));
@@ -145,31 +153,34 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
   }
 }
 
-template <int F, bool B>
-hipError_t launch_dq(const uint8_t* c, const uint8_t* s, void* y, int64_t n, hipStream_t st) {
+template <int F, bool B, bool B2>
+hipError_t launch_dq(const uint8_t* c, const uint8_t* s, void* y, int64_t n, int64_t cols, hipStream_t st) {
   const int64_t chunks = n / 16;
   const int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((mx_dequant_kernel<F, B>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, c, s, y,
-                     chunks);
+  hipLaunchKernelGGL((mx_dequant_kernel<F, B, B2>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, c, s, y,
+                     chunks, cols);
   return hipGetLastError();
 }
 
 template <int F>
-hipError_t by_out(bool out_bf16, const uint8_t* c, const uint8_t* s, void* y, int64_t n, hipStream_t st) {
-  return out_bf16 ? launch_dq<F, true>(c, s, y, n, st) : launch_dq<F, false>(c, s, y, n, st);
+hipError_t by_out(bool out_bf16, const uint8_t* c, const uint8_t* s, void* y, int64_t n, int64_t cols,
+                  hipStream_t st) {
+  if (cols > 0)
+    return out_bf16 ? launch_dq<F, true, true>(c, s, y, n, cols, st) : launch_dq<F, false, true>(c, s, y, n, cols, st);
+  return out_bf16 ? launch_dq<F, true, false>(c, s, y, n, 0, st) : launch_dq<F, false, false>(c, s, y, n, 0, st);
 }
 
 }  // namespace
 
 hipError_t launch_dequant(int fmt, bool out_bf16, const uint8_t* codes, const uint8_t* scales,
-                          void* y, int64_t n, hipStream_t s) {
+                          void* y, int64_t n, int64_t cols, hipStream_t s) {
   switch (fmt) {
-    case kE4M3: return by_out<kE4M3>(out_bf16, codes, scales, y, n, s);
-    case kE5M2: return by_out<kE5M2>(out_bf16, codes, scales, y, n, s);
-    case kE2M1: return by_out<kE2M1>(out_bf16, codes, scales, y, n, s);
-    case kE2M3: return by_out<kE2M3>(out_bf16, codes, scales, y, n, s);
-    case kE3M2: return by_out<kE3M2>(out_bf16, codes, scales, y, n, s);
-    case kInt8: return by_out<kInt8>(out_bf16, codes, scales, y, n, s);
+    case kE4M3: return by_out<kE4M3>(out_bf16, codes, scales, y, n, cols, s);
+    case kE5M2: return by_out<kE5M2>(out_bf16, codes, scales, y, n, cols, s);
+    case kE2M1: return by_out<kE2M1>(out_bf16, codes, scales, y, n, cols, s);
+    case kE2M3: return by_out<kE2M3>(out_bf16, codes, scales, y, n, cols, s);
+    case kE3M2: return by_out<kE3M2>(out_bf16, codes, scales, y, n, cols, s);
+    case kInt8: return by_out<kInt8>(out_bf16, codes, scales, y, n, cols, s);
     default: return hipErrorInvalidValue;
   }
 }

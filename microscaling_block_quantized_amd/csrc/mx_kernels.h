@@ -10,18 +10,20 @@ namespace mx {
 // One quantize launch over a dense [batch][rows][cols] tensor.
 struct CastArgs {
   const void* x;          // BF16 or FP32 elements
-  void* row_codes;        // [batch][rows][cols] (E2M1: [..][cols/2]) or null
-  uint8_t* row_scales;    // [batch][rows][cols/32] or null
-  void* col_codes;        // [batch][cols][rows] (E2M1: [..][rows/2]) or null
-  uint8_t* col_scales;    // [batch][cols][rows/32] or null
+  void* row_codes;        // [batch][rows][cols * bits / 8] or null
+  uint8_t* row_scales;    // [batch][rows][cols/32] (32x32 blocks: [batch][rows/32][cols/32]) or null
+  void* col_codes;        // [batch][cols][rows * bits / 8] or null
+  uint8_t* col_scales;    // [batch][cols][rows/32] (32x32 blocks: [batch][cols/32][rows/32]) or null
   int64_t rows, cols;     // per batch slice
   int64_t elements;       // batch * rows * cols
   uint32_t tiles_r, tiles_c;
   uint32_t flags;         // kRowScaleDword / kColScaleDword
+  uint32_t seed_lo, seed_hi;   // Philox key of stochastic rounding
 };
 
 // A tile's 4 scale bytes per row (column) may be stored as one dword: the
 // plane's row pitch is a multiple of 4 bytes and its base is 4-byte aligned.
+// With 32x32 blocks the pitches are C/32 (row copy) and R/32 (column copy).
 constexpr uint32_t kRowScaleDword = 1u;
 constexpr uint32_t kColScaleDword = 2u;
 
@@ -29,13 +31,24 @@ struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;
 };
 
-// Launch geometry; `blocks` bounds the workgroup count of the chosen kernel.
-CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, int axis);
+// Launch geometry; `blocks` bounds the workgroup count of the chosen kernel:
+// the row-only stream kernel (row_stream) or the tiled one.
+CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, bool row_stream);
+// Round-to-nearest-even, 1x32 blocks.
 hipError_t launch_cast(bool in_bf16, int fmt, int mode, int axis, const CastArgs& a,
                        uint32_t nblocks, hipStream_t s);
+// Round-to-nearest-even, 32x32 blocks (always the tiled kernel).
+hipError_t launch_cast_2d(bool in_bf16, int fmt, int mode, int axis, const CastArgs& a,
+                          uint32_t nblocks, hipStream_t s);
+// Stochastic rounding, 1x32 or 32x32 blocks.
+hipError_t launch_cast_sr(bool in_bf16, int fmt, int mode, int axis, bool blocks_2d, const CastArgs& a,
+                          uint32_t nblocks, hipStream_t s);
 
-// Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order.
+// Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
+// or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale
+// of element (r, c): scales[(r / 32) * (cols / 32) + c / 32], r counting
+// across the batch).
 hipError_t launch_dequant(int fmt, bool out_bf16, const uint8_t* codes, const uint8_t* scales,
-                          void* y, int64_t n, hipStream_t s);
+                          void* y, int64_t n, int64_t cols, hipStream_t s);
 
 }  // namespace mx

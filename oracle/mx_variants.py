@@ -67,14 +67,16 @@ def philox4x32_10(ctr: np.ndarray, key) -> np.ndarray:
     return np.stack([v.astype(np.uint32) for v in c], axis=-1)
 
 
-def sr_bits(seed: int, n: int) -> np.ndarray:
-    """16 random bits for each of the flat elements 0 .. n-1 (uint16 [n])."""
-    ng = (n + 7) // 8
-    g = np.arange(ng, dtype=np.uint64)
+def sr_bits(seed: int, n: int, start: int = 0) -> np.ndarray:
+    """16 random bits for each of the flat elements start .. start+n-1 (uint16 [n])."""
+    g0 = start >> 3
+    ng = ((start + n + 7) >> 3) - g0
+    g = np.arange(g0, g0 + ng, dtype=np.uint64)
     ctr = np.stack([g & _MASK, g >> np.uint64(32), np.zeros_like(g), np.zeros_like(g)], axis=-1)
     words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))   # [ng, 4]
     halves = np.stack([words & 0xFFFF, words >> 16], axis=-1).astype(np.uint16)   # [ng, 4, 2]
-    return halves.reshape(-1)[:n]
+    off = start - 8 * g0
+    return halves.reshape(-1)[off:off + n]
 
 
 def _spacing(a: np.ndarray, fmt: Fmt) -> np.ndarray:
@@ -136,19 +138,21 @@ def _quant_plane(x64: np.ndarray, u: np.ndarray | None, fmt: Fmt, mode: int, blo
 
 
 def quantize_ex(x: np.ndarray, in_dtype: str, fmt: Fmt, mode: int, axis: int, rounding: str = RNE,
-                seed: int = 0, block: str = BLOCK_1X32) -> dict:
+                seed: int = 0, block: str = BLOCK_1X32, first: int = 0) -> dict:
     """quantize() with a rounding rule (RNE or SR) and a block shape (1x32 or 32x32).
 
     With RNE and 1x32 blocks it computes exactly what mx_oracle.quantize does.
     Returns row_codes/row_scales and/or col_codes/col_scales; the column copy is
     the same quantization of X^T, with each element keeping its random bits.
+    ``first`` is the flat index of x's first element in a larger tensor of which
+    x is a run of whole rows (its SR draws follow that tensor's order).
     """
     x64 = widen(x, in_dtype)
     if x64.ndim == 2:
         x64 = x64[None]
     u = None
     if rounding == SR:
-        u = sr_bits(seed, x64.size).reshape(x64.shape)
+        u = sr_bits(seed, x64.size, first).reshape(x64.shape)
     elif rounding != RNE:
         raise ValueError(f"unknown rounding {rounding!r}")
     out = {}

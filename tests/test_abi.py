@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10100
+    assert mxb.mx_version() == 10200
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -122,3 +122,37 @@ def test_python_binding_rejects_cpu_tensors():
         mxb.mx_quantize(torch.zeros(32, 32, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         mxb.mx_dequantize(torch.zeros(32, dtype=torch.uint8), torch.zeros(1, dtype=torch.uint8), "e4m3", (1, 32))
+
+
+def qx(lib, opts=None, x=X, dt=1, shape=(1, 64, 64), fmt=0, mode=0, axis=3, rc=RC, rs=RS, cc=CC, cs=CS):
+    v = lambda p: ctypes.c_void_p(p)
+    o = ctypes.byref(opts) if opts is not None else None
+    return lib.mx_quantize_ex(v(x), dt, MxShape(*shape), fmt, mode, axis, o, v(rc), v(rs), v(cc), v(cs), None)
+
+
+def test_quantize_ex_argument_errors(lib):
+    O = mxb.MxQuantOpts
+    assert qx(lib, O(2, 0, 0)) == E_ENUM                 # unknown rounding
+    assert qx(lib, O(0, 2, 0)) == E_ENUM                 # unknown block shape
+    assert qx(lib, O(1, 0, 5), fmt=9) == E_ENUM
+    # 32x32 blocks need rows % 32 == 0 even for the row copy alone
+    assert qx(lib, O(0, 1, 0), axis=1, cc=0, cs=0, shape=(1, 48, 64)) == E_SHAPE
+    assert qx(lib, O(0, 0, 0), axis=1, cc=0, cs=0, shape=(1, 48, 64)) != E_SHAPE
+    assert qx(lib, O(1, 1, 0), rc=X + 1024) == E_ALIAS
+    # a 32x32 scale plane is batch*rows*cols/1024 bytes: 4 bytes here, so RS + 4 is free
+    assert qx(lib, O(0, 1, 0), shape=(1, 64, 64), cs=RS + 4, axis=3) != E_ALIAS
+    assert qx(lib, O(0, 0, 0), shape=(1, 64, 64), cs=RS + 4, axis=3) == E_ALIAS
+    assert qx(lib, O(1, 1, 0), x=0) == E_NULL
+    assert qx(lib, O(1, 0, 0), x=X + 8) == E_ALIGN
+
+
+def test_dequantize_ex_argument_errors(lib):
+    v = lambda p: ctypes.c_void_p(p)
+    dq = lambda block=1, c=CC, s=CS, fmt=0, shape=(1, 64, 64), dt=0, y=Y: lib.mx_dequantize_ex(
+        v(c), v(s), fmt, MxShape(*shape), block, dt, v(y), None)
+    assert dq(block=2) == E_ENUM
+    assert dq(shape=(1, 48, 64)) == E_SHAPE               # 32x32 blocks: rows % 32
+    assert dq(shape=(1, 64, 40)) == E_SHAPE
+    assert dq(c=0) == E_NULL
+    assert dq(y=CC + 16) == E_ALIAS
+    assert dq(c=CC + 2, fmt=3) == E_ALIGN

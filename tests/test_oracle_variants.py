@@ -45,8 +45,9 @@ def test_sr_bits_layout_against_known_answer():
     assert O.sr_bits(0, 8).tolist() == exp
     # the seed is the key: key (0xFFFFFFFF, 0xFFFFFFFF) with counter 0 differs from seed 0
     assert O.sr_bits((1 << 64) - 1, 8).tolist() != exp
-    # element 8 starts counter 1
+    # element 8 starts counter 1; a window of the stream is the same bits
     assert O.sr_bits(0, 16)[:8].tolist() == exp
+    assert np.array_equal(O.sr_bits(7, 40)[5:29], O.sr_bits(7, 24, start=5))
 
 
 # ---------------- stochastic rounding ----------------
