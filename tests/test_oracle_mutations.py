@@ -283,3 +283,41 @@ def test_pins_catch_2d_scale_from_first_row():
         return codes, scales_f
     with planted_v("_quant_plane", plane):
         assert any_pin_fails([(PV.test_2d_scale_is_max_of_row_block_scales, (O.E4M3, O.FLOOR))])
+
+
+# ---- NVFP4 ----
+
+import oracle.nvfp4 as NV  # noqa: E402
+import test_oracle_nvfp4 as PN  # noqa: E402
+
+
+@contextlib.contextmanager
+def planted_nv(name, fn):
+    old = getattr(NV, name)
+    setattr(NV, name, fn)
+    setattr(O, name, fn)
+    try:
+        yield
+    finally:
+        setattr(NV, name, old)
+        setattr(O, name, old)
+
+
+def test_pins_catch_nvfp4_global_scale_without_the_6():
+    def g448(x64):
+        b = x64.shape[0]
+        a = np.abs(np.where(np.isfinite(x64), x64, 0.0)).reshape(b, -1).max(axis=1)
+        return a.astype(np.float32) / np.float32(448.0)
+    with planted_nv("nvfp4_global_scale", g448):
+        assert any_pin_fails([(PN.test_global_scale_is_amax_over_6_times_448, ()),
+                              (PN.test_block_holding_the_tensor_max_decodes_exactly, ())])
+
+
+def test_pins_catch_nvfp4_elements_scaled_without_global():
+    orig = NV._quant_plane
+
+    def no_global(x64, g):
+        return orig(x64, np.ones_like(g))
+    with planted_nv("_quant_plane", no_global):
+        assert any_pin_fails([(PN.test_block_holding_the_tensor_max_decodes_exactly, ()),
+                              (PN.test_scale_steps_match_torch_float32, ())])
