@@ -196,6 +196,31 @@ def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc, rounding="rne", b
     return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "config": cfg}
 
 
+def _nvfp4_workload():
+    """16384x4096 BF16 activations -> NVFP4, both copies, global scale computed
+    in the same call (its amax pass reads the input a second time)."""
+    b, r, c = 1, ROWS, COLS
+    n = b * r * c
+    nbytes = 2 * n * 2 + 2 * (n // 2 + n // 16) + 4
+
+    def make(dev, i):
+        import torch
+        import microscaling_block_quantized_amd as mx
+        import mx_inputs as I
+        x = I.activations(r, c, seed=1 + i, device=dev).view(b, r, c)
+        out = {"global_scale": torch.empty((b,), dtype=torch.float32, device=dev),
+               "row_codes": torch.empty((b, r, c // 2), dtype=torch.uint8, device=dev),
+               "row_scales": torch.empty((b, r, c // 16), dtype=torch.uint8, device=dev),
+               "col_codes": torch.empty((b, c, r // 2), dtype=torch.uint8, device=dev),
+               "col_scales": torch.empty((b, c, r // 16), dtype=torch.uint8, device=dev)}
+        return mx.BoundQuantizeNvfp4(x, "both", out)
+    desc = ("activations 16384x4096 bf16 -> NVFP4 (E2M1, 16-element UE4M3 blocks, FP32 global scale) row+col, "
+            "global scale computed in the call")
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+            "config": {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": "nvfp4", "axis": "both",
+                       "input_reads": 2}}
+
+
 def _wide_range_pipeline():
     """64 x 4096x14336 BF16: fused E4M3 quantize, then both planes dequantized to BF16."""
     b, r, c = 64, 4096, 14336
@@ -286,6 +311,7 @@ WORKLOADS = {
     "weights_2d_e2m1": _cast_workload(_gen("weights"), 1, 14336, 4096, 2, "e2m1", "floor", "both",
                                       "weights 14336x4096 bf16 -> MXFP4 E2M1 32x32 blocks, row+col fused, "
                                       "floor scale rule", block="32x32"),
+    "act_nvfp4": _nvfp4_workload(),
     "wide_range": _wide_range_pipeline(),
     "fp32_normal": _fp32_normal_round_trip(),
 }

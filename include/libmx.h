@@ -103,8 +103,8 @@ typedef struct {
 
 #define MX_OK 0
 #define MX_ERR_NULL (-1)        /* a required pointer is NULL, or an unused one is not */
-#define MX_ERR_SHAPE (-2)       /* non-positive extent, or a blocked extent % 32 != 0 */
-#define MX_ERR_ALIGN (-3)       /* x, codes or y not 16-byte aligned */
+#define MX_ERR_SHAPE (-2)       /* non-positive extent, or a blocked extent not a multiple of the block */
+#define MX_ERR_ALIGN (-3)       /* a pointer without the alignment its call requires */
 #define MX_ERR_ENUM (-4)        /* unknown fmt / mode / dtype / axis */
 #define MX_ERR_ALIAS (-5)       /* input and an output overlap, or two outputs do */
 #define MX_ERR_TOO_LARGE (-6)   /* beyond one launch: cols >= 2^22, rows >= 2^23 with
@@ -161,6 +161,37 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
  * must be 0. MX_BLOCK_1X32 is exactly mx_dequantize. */
 int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape s, mx_block block,
                      mx_dtype y_dtype, void* y, void* stream);
+
+/* NVFP4 (same article, §3, the §4 table and §7): E2M1 elements (MXFP4's) in
+ * blocks of 16, each with an unsigned E4M3 (UE4M3, at most 448, sign bit 0)
+ * block scale, and one FP32 global scale per tensor (per batch slice) equal
+ * to the slice's largest finite magnitude A over 6 * 448; 4.5 bits per
+ * element. Every step is one FP32 operation with round-to-nearest-even, in
+ * this order: g = A / 2688; t = (amax_b / 6) / g -> UE4M3 (saturating at
+ * 448); r_b = 1 / (s_b * g); q = x * r_b -> E2M1 (saturating at 6). A block
+ * whose scale code is 0 or whose r_b is not finite, and every block when
+ * g == 0, stores codes 0; a block holding NaN or Inf stores scale 0x7F (UE4M3
+ * NaN) and codes 0.
+ *   global_scale  [batch] FP32, device memory: written (global_given == 0)
+ *                 or read (global_given == 1, e.g. a scale kept from an
+ *                 earlier step)
+ *   row_codes     [batch][rows][cols/2] (element 2k in bits 3:0)
+ *   row_scales    [batch][rows][cols/16] UE4M3 bytes
+ *   col_codes     [batch][cols][rows/2]  (the same cast of X^T)
+ *   col_scales    [batch][cols][rows/16]
+ * Shape: cols % 16 == 0, rows % 16 == 0 with MX_AXIS_COL, batch <= 65535.
+ * x, row_codes and col_codes 16-byte aligned, global_scale 4-byte aligned.
+ * Computing g reads x once more than the cast (one extra pass). */
+int mx_quantize_nvfp4(const void* x, mx_dtype x_dtype, mx_shape s, mx_axis axis, float* global_scale,
+                      int global_given, void* row_codes, uint8_t* row_scales, void* col_codes,
+                      uint8_t* col_scales, void* stream);
+
+/* NVFP4 dequantization of one plane ([batch][rows][cols] as stored, blocks of
+ * 16 along cols): y = (e2m1 * ue4m3) * g in FP32 (the first product is exact),
+ * BF16 output rounded to nearest-even from that FP32 value; a NaN block scale
+ * gives the canonical NaN. codes 8-byte aligned, y 16-byte aligned. */
+int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* global_scale, mx_shape s,
+                        mx_dtype y_dtype, void* y, void* stream);
 
 /* Static text for an MX_* code; never NULL. */
 const char* mx_strerror(int err);

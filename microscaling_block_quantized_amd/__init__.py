@@ -9,6 +9,7 @@ The functions mirror the C ABI in ``include/libmx.h``:
                                             (mx_quantize_ex when rounding or block
                                             is not the default)
     mx_dequantize(codes, scales, fmt, shape, out_dtype, block)
+    mx_quantize_nvfp4(x, axis, global_scale) / mx_dequantize_nvfp4(...)
     mx_plane_bytes(fmt, shape)           -> (code bytes, scale bytes) of one plane
     mx_strerror(err), mx_version()
 
@@ -22,7 +23,8 @@ import os
 
 __all__ = [
     "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "ROUNDING", "BLOCK", "MxQuantOpts", "lib_path", "load", "mx_version", "mx_strerror",
-    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "EXPORTS", "BoundQuantize", "BoundDequantize",
+    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "EXPORTS",
+    "BoundQuantize", "BoundDequantize", "BoundQuantizeNvfp4",
 ]
 
 FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4, "int8": 5}
@@ -33,7 +35,7 @@ ROUNDING = {"rne": 0, "sr": 1}
 BLOCK = {"1x32": 0, "32x32": 1}
 DTYPE = {"f32": 0, "bf16": 1}
 EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_quantize_ex", "mx_dequantize", "mx_dequantize_ex",
-           "mx_strerror", "mx_version")
+           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_strerror", "mx_version")
 
 _LIB = None
 
@@ -83,6 +85,10 @@ def load() -> ctypes.CDLL:
                                    u8p, vp]
     lib.mx_dequantize_ex.restype = i32
     lib.mx_dequantize_ex.argtypes = [vp, u8p, i32, MxShape, i32, i32, vp, vp]
+    lib.mx_quantize_nvfp4.restype = i32
+    lib.mx_quantize_nvfp4.argtypes = [vp, i32, MxShape, i32, vp, i32, vp, u8p, vp, u8p, vp]
+    lib.mx_dequantize_nvfp4.restype = i32
+    lib.mx_dequantize_nvfp4.argtypes = [vp, u8p, vp, MxShape, i32, vp, vp]
     _LIB = lib
     return lib
 
@@ -252,3 +258,89 @@ class BoundDequantize:
         err = self._fn(*self._args)
         if err:
             raise MXError(err, "mx_dequantize")
+
+
+def _nv_planes(x, axis: str, out: dict | None):
+    import torch
+    b, r, c = _shape3(x.shape)
+    ax = AXIS[axis]
+    out = out or {}
+    dev = x.device
+
+    def plane(name, shp, dt=torch.uint8):
+        t = out.get(name)
+        return t if t is not None else torch.empty(shp, dtype=dt, device=dev)
+
+    planes = {"global_scale": plane("global_scale", (b,), torch.float32)}
+    if ax & 1:
+        planes["row_codes"] = plane("row_codes", (b, r, c // 2))
+        planes["row_scales"] = plane("row_scales", (b, r, c // 16))
+    if ax & 2:
+        planes["col_codes"] = plane("col_codes", (b, c, r // 2))
+        planes["col_scales"] = plane("col_scales", (b, c, max(r // 16, 1)))
+    return planes
+
+
+def mx_quantize_nvfp4(x, axis: str = "both", global_scale=None, out: dict | None = None):
+    """NVFP4 cast of a GPU tensor [R][C] or [B][R][C] (bfloat16 or float32).
+
+    Returns {"global_scale" [B] float32, "row_codes" [B][R][C/2], "row_scales"
+    [B][R][C/16], "col_codes" [B][C][R/2], "col_scales" [B][C][R/16]} (planes of
+    the requested axes; batch axis dropped for a 2-D input, except in
+    global_scale). A given ``global_scale`` tensor is used as is instead of the
+    tensor's own amax / (6 * 448).
+    """
+    import torch
+    if not x.is_cuda:
+        raise ValueError("mx_quantize_nvfp4 needs a GPU tensor (libmx has no CPU path)")
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_contiguous():
+        raise TypeError("input must be a contiguous bfloat16 or float32 tensor")
+    b, r, c = _shape3(x.shape)
+    out = dict(out or {})
+    given = global_scale is not None
+    if given:
+        out["global_scale"] = global_scale
+    planes = _nv_planes(x, axis, out)
+    with torch.cuda.device(x.device):
+        err = load().mx_quantize_nvfp4(
+            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), AXIS[axis],
+            _ptr(planes["global_scale"]), int(given), _ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")),
+            _ptr(planes.get("col_codes")), _ptr(planes.get("col_scales")), _stream_of(x))
+    if err:
+        raise MXError(err, "mx_quantize_nvfp4")
+    if x.dim() == 2:
+        planes = {k: (v if k == "global_scale" else v[0]) for k, v in planes.items()}
+    return planes
+
+
+def mx_dequantize_nvfp4(codes, scales, global_scale, shape, out_dtype: str = "f32", out=None):
+    """Dequantize one NVFP4 plane; ``shape`` is its element shape as stored."""
+    import torch
+    b, r, c = _shape3(shape)
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=codes.device)
+    with torch.cuda.device(codes.device):
+        err = load().mx_dequantize_nvfp4(_ptr(codes), _ptr(scales), _ptr(global_scale), MxShape(b, r, c),
+                                         DTYPE[out_dtype], _ptr(y), _stream_of(codes))
+    if err:
+        raise MXError(err, "mx_dequantize_nvfp4")
+    return y
+
+
+class BoundQuantizeNvfp4:
+    """An mx_quantize_nvfp4 call marshalled once (see BoundQuantize)."""
+
+    def __init__(self, x, axis: str, out: dict, global_given: bool = False):
+        import torch
+        b, r, c = _shape3(x.shape)
+        self._fn = load().mx_quantize_nvfp4
+        self._args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), AXIS[axis],
+                      _ptr(out["global_scale"]), int(global_given), _ptr(out.get("row_codes")),
+                      _ptr(out.get("row_scales")), _ptr(out.get("col_codes")), _ptr(out.get("col_scales")),
+                      _stream_of(x))
+        self._keep = (x, out)
+
+    def __call__(self) -> None:
+        err = self._fn(*self._args)
+        if err:
+            raise MXError(err, "mx_quantize_nvfp4")

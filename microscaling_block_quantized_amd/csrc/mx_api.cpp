@@ -55,14 +55,14 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10200; }
+int mx_version(void) { return 10300; }
 
 const char* mx_strerror(int err) {
   switch (err) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "a required pointer is NULL, or a pointer of an unused axis is not";
-    case MX_ERR_SHAPE: return "invalid shape: extents must be >= 1 and blocked extents multiples of 32";
-    case MX_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case MX_ERR_SHAPE: return "invalid shape: extents must be >= 1 and blocked extents multiples of the block";
+    case MX_ERR_ALIGN: return "a data pointer is not aligned as required";
     case MX_ERR_ENUM: return "unknown format, scale mode, dtype or axis";
     case MX_ERR_ALIAS: return "input and output buffers overlap";
     case MX_ERR_TOO_LARGE: return "tensor too large for one launch";
@@ -175,6 +175,77 @@ int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_sh
   if ((n / 16 + 255) / 256 > kMaxGrid) return MX_ERR_TOO_LARGE;
   const hipError_t e = mx::launch_dequant(int(fmt), y_dtype == MX_BF16, static_cast<const uint8_t*>(codes),
                                           scales, y, n, b2d ? s.cols : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_quantize_nvfp4(const void* x, mx_dtype x_dtype, mx_shape s, mx_axis axis, float* global_scale,
+                      int global_given, void* row_codes, uint8_t* row_scales, void* col_codes,
+                      uint8_t* col_scales, void* stream) {
+  constexpr int64_t kNv = 16;
+  if (!valid_dtype(x_dtype) || !valid_axis(axis) || (global_given != 0 && global_given != 1)) return MX_ERR_ENUM;
+  const bool want_row = (axis & MX_AXIS_ROW) != 0;
+  const bool want_col = (axis & MX_AXIS_COL) != 0;
+  if (x == nullptr || global_scale == nullptr) return MX_ERR_NULL;
+  if (want_row != (row_codes != nullptr) || want_row != (row_scales != nullptr)) return MX_ERR_NULL;
+  if (want_col != (col_codes != nullptr) || want_col != (col_scales != nullptr)) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kNv != 0 || (want_col && s.rows % kNv != 0)) return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(global_scale, 4) || (want_row && !aligned(row_codes, 16)) ||
+      (want_col && !aligned(col_codes, 16)))
+    return MX_ERR_ALIGN;
+  Range rs[6];
+  int nr = 0;
+  rs[nr++] = range_of(x, n * (x_dtype == MX_BF16 ? 2 : 4));
+  rs[nr++] = range_of(global_scale, s.batch * 4);
+  if (want_row) { rs[nr++] = range_of(row_codes, n / 2); rs[nr++] = range_of(row_scales, n / kNv); }
+  if (want_col) { rs[nr++] = range_of(col_codes, n / 2); rs[nr++] = range_of(col_scales, n / kNv); }
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
+  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, false);
+  if (g.blocks > kMaxGrid || s.batch > 65535) return MX_ERR_TOO_LARGE;
+  if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;
+
+  mx::NvArgs a;
+  a.x = x;
+  a.row_codes = row_codes;
+  a.row_scales = row_scales;
+  a.col_codes = col_codes;
+  a.col_scales = col_scales;
+  a.global_scale = global_scale;
+  a.rows = s.rows;
+  a.cols = s.cols;
+  a.tiles_r = uint32_t(g.tiles_r);
+  a.tiles_c = uint32_t(g.tiles_c);
+  a.flags = 0;
+  if (want_row && s.cols % 64 == 0 && aligned(row_scales, 4)) a.flags |= mx::kRowScaleDword;
+  if (want_col && s.rows % 64 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = x_dtype == MX_BF16;
+  if (!global_given) {
+    const hipError_t e = mx::launch_nvfp4_global(bf, x, s.batch, s.rows * s.cols, global_scale, st);
+    if (e != hipSuccess) return MX_ERR_LAUNCH;
+  }
+  const hipError_t e = mx::launch_nvfp4_cast(bf, int(axis), a, uint32_t(g.blocks), st);
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* global_scale, mx_shape s,
+                        mx_dtype y_dtype, void* y, void* stream) {
+  constexpr int64_t kNv = 16;
+  if (!valid_dtype(y_dtype)) return MX_ERR_ENUM;
+  if (codes == nullptr || scales == nullptr || global_scale == nullptr || y == nullptr) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kNv != 0) return MX_ERR_SHAPE;
+  if (!aligned(codes, 8) || !aligned(y, 16) || !aligned(global_scale, 4)) return MX_ERR_ALIGN;
+  const Range ry = range_of(y, n * (y_dtype == MX_BF16 ? 2 : 4));
+  if (overlap(ry, range_of(codes, n / 2)) || overlap(ry, range_of(scales, n / kNv)) ||
+      overlap(ry, range_of(global_scale, s.batch * 4)))
+    return MX_ERR_ALIAS;
+  if ((n / kNv + 255) / 256 > kMaxGrid) return MX_ERR_TOO_LARGE;
+  const hipError_t e = mx::launch_nvfp4_dequant(y_dtype == MX_BF16, static_cast<const uint8_t*>(codes), scales,
+                                                global_scale, y, n / kNv, s.rows * s.cols / kNv,
+                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 

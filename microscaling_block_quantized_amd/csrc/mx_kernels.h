@@ -44,6 +44,27 @@ hipError_t launch_cast_2d(bool in_bf16, int fmt, int mode, int axis, const CastA
 hipError_t launch_cast_sr(bool in_bf16, int fmt, int mode, int axis, bool blocks_2d, const CastArgs& a,
                           uint32_t nblocks, hipStream_t s);
 
+// One NVFP4 cast over a dense [batch][rows][cols] tensor (mx_nvfp4.hip): E2M1
+// codes two per byte, UE4M3 scales per 16 elements, FP32 global scale per slice.
+struct NvArgs {
+  const void* x;
+  void* row_codes;             // [batch][rows][cols/2] or null
+  uint8_t* row_scales;         // [batch][rows][cols/16] or null
+  void* col_codes;             // [batch][cols][rows/2] or null
+  uint8_t* col_scales;         // [batch][cols][rows/16] or null
+  const float* global_scale;   // [batch]
+  int64_t rows, cols;
+  uint32_t tiles_r, tiles_c;
+  uint32_t flags;              // kRowScaleDword: cols % 64 == 0; kColScaleDword: rows % 64 == 0
+};
+
+// g[b] = (largest finite |x| of slice b) / 2688 into gs[0 .. batch-1] (three launches).
+hipError_t launch_nvfp4_global(bool in_bf16, const void* x, int64_t batch, int64_t slice_elems, float* gs,
+                               hipStream_t s);
+hipError_t launch_nvfp4_cast(bool in_bf16, int axis, const NvArgs& a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_nvfp4_dequant(bool out_bf16, const uint8_t* codes, const uint8_t* scales, const float* gs,
+                                void* y, int64_t nblocks, int64_t blocks_per_slice, hipStream_t s);
+
 // Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
 // or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale
 // of element (r, c): scales[(r / 32) * (cols / 32) + c / 32], r counting

@@ -18,11 +18,12 @@ those steps with numpy float32 operations, one at a time:
     slice); g = fp32(A / 2688) is the global (decode) scale.
   * Block scale: t = fp32(fp32(amax_b / 6) / g), encoded as E4M3 with
     round-to-nearest-even, saturating at 448, sign bit 0 (UE4M3).
-  * Elements: q = fp32(x / fp32(s_b * g)) with s_b the decoded block scale,
+  * Elements: q = fp32(x * r_b) with r_b = fp32(1 / fp32(s_b * g)) and s_b the
+    decoded block scale (the §4 table applies NVFP4's scales by multiplication),
     encoded as E2M1 with round-to-nearest-even and saturation at 6.
   * A block whose scale code is 0 (all-zero blocks, and blocks too small for
-    UE4M3 relative to g), whose fp32(s_b * g) underflows to 0, and every block
-    of a tensor with g == 0, store codes 0.
+    UE4M3 relative to g), whose r_b is not finite (fp32(s_b * g) is 0 or below
+    2^-128), and every block of a tensor with g == 0, store codes 0.
   * A block holding NaN or +-Inf gets the UE4M3 NaN code 0x7F and element codes 0;
     A ignores non-finite elements.
   * Decoding: y = fp32(fp32(e2m1 * ue4m3) * g) (the first product is exact);
@@ -79,8 +80,9 @@ def _quant_plane(x64: np.ndarray, g: np.ndarray):
     sval = _f32(value_table(E4M3)[scode])
     den = sval * gg                                             # FP32 product
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        q = _f32(clean) / den[..., None]                        # FP32 division
-    zero = ((scode == 0) | (den == 0))[..., None]             # den can underflow for a tiny g
+        rb = np.float32(1) / den                                # FP32 division
+        q = _f32(clean) * rb[..., None]                         # FP32 product
+    zero = ((scode == 0) | ~np.isfinite(rb))[..., None]       # r_b overflows for a tiny s_b * g
     q = np.where(zero, np.float32(0), q)
     codes = encode_elements(q.astype(np.float64), E2M1)
     codes = np.where(zero, 0, codes).astype(np.uint8)

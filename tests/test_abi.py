@@ -1,7 +1,10 @@
 """The C ABI on the host: exported symbols, plane sizes and argument errors.
 
-None of these calls reaches a GPU: every error path returns before the first
-HIP call, and only error paths are exercised here.
+None of these calls reaches a GPU: every call here fails validation, which
+returns before the first HIP call. The addresses are fake, so a call that
+passed validation would launch a kernel on them; to show that a check lets a
+case through, a test makes a later check fail instead (an alias, or an
+oversized extent).
 """
 import ctypes
 import os
@@ -36,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10200
+    assert mxb.mx_version() == 10300
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -137,11 +140,16 @@ def test_quantize_ex_argument_errors(lib):
     assert qx(lib, O(1, 0, 5), fmt=9) == E_ENUM
     # 32x32 blocks need rows % 32 == 0 even for the row copy alone
     assert qx(lib, O(0, 1, 0), axis=1, cc=0, cs=0, shape=(1, 48, 64)) == E_SHAPE
-    assert qx(lib, O(0, 0, 0), axis=1, cc=0, cs=0, shape=(1, 48, 64)) != E_SHAPE
+    # 1x32 blocks accept 48 rows for the row copy: the alias check after it fails
+    assert qx(lib, O(0, 0, 0), axis=1, cc=0, cs=0, shape=(1, 48, 64), rc=X + 1024) == E_ALIAS
     assert qx(lib, O(1, 1, 0), rc=X + 1024) == E_ALIAS
-    # a 32x32 scale plane is batch*rows*cols/1024 bytes: 4 bytes here, so RS + 4 is free
-    assert qx(lib, O(0, 1, 0), shape=(1, 64, 64), cs=RS + 4, axis=3) != E_ALIAS
-    assert qx(lib, O(0, 0, 0), shape=(1, 64, 64), cs=RS + 4, axis=3) == E_ALIAS
+    # a 32x32 scale plane is batch*rows*cols/1024 bytes: for 64 x 2^22 elements that is
+    # 256 KiB, so a column scale plane right after it does not overlap (then the
+    # cols >= 2^22 check fails), while the 8 MiB of 1x32 row scales would overlap it
+    G = 1 << 32
+    big = dict(shape=(1, 64, 1 << 22), x=G, rc=2 * G, rs=3 * G, cc=4 * G, cs=3 * G + (1 << 18), axis=3)
+    assert qx(lib, O(0, 1, 0), **big) == E_BIG
+    assert qx(lib, O(0, 0, 0), **big) == E_ALIAS
     assert qx(lib, O(1, 1, 0), x=0) == E_NULL
     assert qx(lib, O(1, 0, 0), x=X + 8) == E_ALIGN
 
@@ -156,3 +164,32 @@ def test_dequantize_ex_argument_errors(lib):
     assert dq(c=0) == E_NULL
     assert dq(y=CC + 16) == E_ALIAS
     assert dq(c=CC + 2, fmt=3) == E_ALIGN
+
+
+def test_nvfp4_argument_errors(lib):
+    v = lambda p: ctypes.c_void_p(p)
+    G = 0x70000000
+
+    def nq(x=X, dt=1, shape=(1, 64, 64), axis=3, gs=G, given=0, rc=RC, rs=RS, cc=CC, cs=CS):
+        return lib.mx_quantize_nvfp4(v(x), dt, MxShape(*shape), axis, v(gs), given, v(rc), v(rs), v(cc), v(cs), None)
+    assert nq(dt=3) == E_ENUM
+    assert nq(axis=0) == E_ENUM
+    assert nq(given=2) == E_ENUM
+    assert nq(gs=0) == E_NULL
+    assert nq(axis=1) == E_NULL
+    assert nq(shape=(1, 64, 40)) == E_SHAPE                      # cols % 16
+    assert nq(shape=(1, 40, 64)) == E_SHAPE                      # rows % 16 with a column copy
+    # the row copy alone accepts 40 rows: the alias check after it fails
+    assert nq(shape=(1, 40, 64), axis=1, cc=0, cs=0, rc=X + 64) == E_ALIAS
+    assert nq(gs=G + 2) == E_ALIGN
+    assert nq(x=X + 8) == E_ALIGN
+    assert nq(gs=RS) == E_ALIAS
+    assert nq(shape=(70000, 16, 16)) == E_BIG
+
+    def nd(c=CC, s=CS, gs=G, shape=(1, 64, 64), dt=0, y=Y):
+        return lib.mx_dequantize_nvfp4(v(c), v(s), v(gs), MxShape(*shape), dt, v(y), None)
+    assert nd(dt=7) == E_ENUM
+    assert nd(gs=0) == E_NULL
+    assert nd(shape=(1, 64, 24)) == E_SHAPE
+    assert nd(c=CC + 4) == E_ALIGN
+    assert nd(y=CC + 16) == E_ALIAS

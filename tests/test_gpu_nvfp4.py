@@ -1,0 +1,138 @@
+"""Bit-exact parity of the NVFP4 cast and dequantization (mx_quantize_nvfp4,
+mx_dequantize_nvfp4) with the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mx_inputs as I
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+OAXIS = {"row": O.ROW, "col": O.COL, "both": O.BOTH}
+
+
+def gpu(mx, x, axis, **kw):
+    out = mx.mx_quantize_nvfp4(x.cuda().contiguous(), axis, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def oracle(x, axis, global_scale=None):
+    dt = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    out = O.nvfp4_quantize(I.to_bits(x), dt, OAXIS[axis], global_scale)
+    if x.dim() == 2:
+        out = {k: (v if k == "global_scale" else v[0]) for k, v in out.items()}
+    return out
+
+
+def same(got, exp, what):
+    assert set(got) == set(exp), (got.keys(), exp.keys())
+    for k in exp:
+        g, e = got[k], exp[k]
+        if k == "global_scale":
+            g, e = g.view(np.uint32), np.asarray(e, np.float32).view(np.uint32)
+        assert g.shape == e.shape, (what, k, g.shape, e.shape)
+        bad = np.argwhere(g != e)
+        if bad.size:
+            idx = tuple(bad[0])
+            raise AssertionError(f"{what} {k}: {len(bad)} mismatches, first at {idx}: "
+                                 f"gpu={g[idx]:#x} oracle={e[idx]:#x}")
+
+
+def check(mx, x, axis, what=""):
+    same(gpu(mx, x, axis), oracle(x, axis), what)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("axis", ["row", "col", "both"])
+def test_shapes_and_ragged_tails(mx, axis, dt):
+    g = torch.Generator().manual_seed(61)
+    for b, r, c in [(1, 16, 16), (2, 48, 80), (1, 128, 256), (3, 144, 272), (1, 272, 4112), (2, 80, 64)]:
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-10, 10, (b, r, 1), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
+        check(mx, x, axis, f"{(b, r, c)}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_edges_specials_and_zero(mx, dt):
+    x = I.fp32_edges("e2m1")
+    x = x.to(torch.bfloat16) if dt == "bf16" else x
+    x = x[: (x.shape[0] // 16) * 16]
+    check(mx, x, "row", "edges/row")
+    check(mx, x.T.contiguous(), "both", "edges/both")
+    check(mx, torch.zeros((2, 32, 64), dtype=x.dtype), "both", "zeros")
+    grads = I.gradients(144, 96, seed=62)
+    assert not torch.isfinite(grads).all()
+    check(mx, grads, "both", "grads")
+
+
+def test_wide_dynamic_range(mx):
+    """Blocks far below the tensor max fall under UE4M3's range and store zeros."""
+    x = torch.stack([I.wide_range(i, 96, 320, seed=63) for i in range(2)])
+    check(mx, x, "both", "wide")
+    check(mx, I.weights(352, 288, seed=64), "both", "weights")
+
+
+def test_given_global_scale(mx):
+    x = I.activations(160, 288, seed=65)
+    gs = torch.tensor([0.0371], dtype=torch.float32)
+    out = mx.mx_quantize_nvfp4(x.cuda(), "both", global_scale=gs.cuda())
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    same(got, oracle(x, "both", gs.numpy()), "given")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_dequant_every_code_and_scale(mx, out_dtype):
+    codes = np.tile(np.arange(256, dtype=np.uint8), 512).reshape(1, 2048, 64)   # 128 elements per row
+    rng = np.random.default_rng(66)
+    scales = rng.integers(0, 256, (1, 2048, 8), dtype=np.uint8)
+    scales[0, :128, 0] = np.arange(128)                         # every UE4M3 code, and 0x80.. too
+    scales[0, 128:256, 0] = np.arange(128, 256)
+    for gval in (1.0, 3.1e-5, 7.7e30, 1e-38):
+        gs = np.array([gval], np.float32)
+        y = mx.mx_dequantize_nvfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                   torch.from_numpy(gs).cuda(), (1, 2048, 128), out_dtype)
+        torch.cuda.synchronize()
+        ref = O.nvfp4_dequantize(codes, scales, gs, out_dtype)
+        yb = y.cpu()
+        yb = yb.view(torch.int16).numpy().view(np.uint16) if out_dtype == "bf16" else yb.numpy().view(np.uint32)
+        bad = np.argwhere(yb != ref)
+        assert bad.size == 0, (gval, bad[:3])
+
+
+def test_round_trip_through_both_calls(mx):
+    x = I.activations(256, 512, seed=67)
+    out = mx.mx_quantize_nvfp4(x.cuda(), "both")
+    yr = mx.mx_dequantize_nvfp4(out["row_codes"], out["row_scales"], out["global_scale"], (1, 256, 512), "bf16")
+    yc = mx.mx_dequantize_nvfp4(out["col_codes"], out["col_scales"], out["global_scale"], (1, 512, 256), "f32")
+    torch.cuda.synchronize()
+    exp = oracle(x, "both")
+    same({k: v.cpu().numpy() for k, v in out.items()}, exp, "quant")
+    rr = O.nvfp4_dequantize(exp["row_codes"][None], exp["row_scales"][None], exp["global_scale"], "bf16")[0]
+    rc = O.nvfp4_dequantize(exp["col_codes"][None], exp["col_scales"][None], exp["global_scale"], "f32")[0]
+    got_r = yr.cpu().view(torch.int16).numpy().view(np.uint16)[0]
+    bad = np.argwhere(got_r != rr)
+    assert bad.size == 0, (len(bad), bad[:4], got_r[tuple(bad[0])], rr[tuple(bad[0])])
+    got_c = yc.cpu().numpy().view(np.uint32)[0]
+    bad = np.argwhere(got_c != rc)
+    assert bad.size == 0, (len(bad), bad[:4], got_c[tuple(bad[0])], rc[tuple(bad[0])])
+
+
+def test_full_activations(mx):
+    """16384x4096 BF16 activations, NVFP4 both copies; the global scale from the
+    oracle over the whole tensor, codes and scales on sampled slabs."""
+    R, C = 16384, 4096
+    x = I.activations(R, C, seed=1, device="cuda")
+    out = mx.mx_quantize_nvfp4(x, "both")
+    torch.cuda.synchronize()
+    xc = x.cpu()
+    g = O.nvfp4_global_scale(O.widen(I.to_bits(xc), "bf16")[None])
+    assert out["global_scale"].cpu().numpy().view(np.uint32)[0] == g.view(np.uint32)[0]
+    for r0 in (0, 8192 - 128, R - 256):
+        exp = oracle(xc[r0:r0 + 256], "both", g)
+        assert np.array_equal(out["row_codes"][r0:r0 + 256].cpu().numpy(), exp["row_codes"])
+        assert np.array_equal(out["row_scales"][r0:r0 + 256].cpu().numpy(), exp["row_scales"])
+        assert np.array_equal(out["col_codes"][:, r0 // 2:(r0 + 256) // 2].cpu().numpy(), exp["col_codes"])
+        assert np.array_equal(out["col_scales"][:, r0 // 16:(r0 + 256) // 16].cpu().numpy(), exp["col_scales"])

@@ -78,11 +78,11 @@ def test_scale_steps_match_torch_float32():
     t = (amax / 6.0) / g
     ref = t.clamp(max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(q["row_scales"][0], ref)
-    # elements: fp32(x / fp32(s * g)), RNE onto E2M1 (the pinned MX encoder)
+    # elements: fp32(x * fp32(1 / fp32(s * g))), RNE onto E2M1 (the pinned MX encoder)
     s = ref.astype(np.int64)
     sv = torch.from_numpy(O.value_table(O.E4M3)[s].astype(np.float32))
-    den = (sv * g).repeat_interleave(16, dim=1)
-    qv = (xt / den).numpy().astype(np.float64)
+    rb = (1.0 / (sv * g)).repeat_interleave(16, dim=1)
+    qv = (xt * rb).numpy().astype(np.float64)
     codes = O.encode_elements(qv, O.E2M1)
     codes[np.repeat(s == 0, 16, axis=1)] = 0
     assert np.array_equal(O.unpack_e2m1(q["row_codes"])[0], codes)
