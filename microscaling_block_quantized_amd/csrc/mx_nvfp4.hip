@@ -20,6 +20,17 @@
 // amax with one atomic max per wave into it (as FP32 bits: magnitudes order
 // as unsigned integers), then divide in place. The cast reuses the MX tiled
 // kernel's layout (128 x 256 tiles, 8 waves, LDS-staged column codes).
+//
+// The cast never divides per element and rarely per block:
+//  * r_b depends only on the block's scale code, so each workgroup divides once
+//    per code (256 entries in LDS, shared by the tile).
+//  * The block code is first estimated as fp32(amax_b * k), k = fp32(fp32(1/6) *
+//    fp32(1/g)). Every rounding in the exact and the estimated chain is relative
+//    error at most 2^-24 while amax_b >= 2^-120 and 2^-125 <= g <= 2^100, so the
+//    estimate is within 6 FP32 ulps of the exact t. E4M3 rounding is monotone:
+//    when t - 16 ulps and t + 16 ulps round to the same code, that is the code
+//    of the exact t. Otherwise, or outside those ranges, the block takes the
+//    two IEEE divisions.
 #include "mx_cast_impl.h"
 
 namespace mx {
@@ -28,6 +39,10 @@ namespace {
 
 constexpr float kE2m1Max = 6.0f;
 constexpr float kNvGlobalDiv = 6.0f * 448.0f;      // 2688
+constexpr float kRcp6 = 0x1.555556p-3f;            // fp32(1/6)
+constexpr uint32_t kNvWindow = 16;                 // ulps each side of the estimate
+constexpr uint32_t kNvTcap = 0x49800000u;          // 2^20: every t above 464 saturates alike
+constexpr uint32_t kNvAmin = 0x03800000u;          // 2^-120: amax/6 stays a normal FP32
 
 // ---------------- global scale ----------------
 
@@ -89,25 +104,63 @@ struct NvBlock {
   bool zero;         // store codes 0
 };
 
-// amag: FP32 bits of the block's largest magnitude (>= 0x7F800000: NaN or Inf present)
-__device__ __forceinline__ NvBlock nv_block(uint32_t amag, float g) {
-  NvBlock b;
-  if (amag >= 0x7F800000u) {
-    b.code = 0x7Fu; b.rcp = 0.0f; b.zero = true;
-    return b;
-  }
-  if (g == 0.0f) {
-    b.code = 0u; b.rcp = 0.0f; b.zero = true;
-    return b;
-  }
-  const float one = scale_operand(127u);
+// Per-slice constants of the block-code estimate.
+struct NvScale {
+  float g;           // global (decode) scale
+  float k;           // fp32(fp32(1/6) * fp32(1/g))
+  bool fast;         // 2^-125 <= g <= 2^100: the estimate's error bound holds
+};
+
+__device__ __forceinline__ NvScale nv_scale(float g) {
+  NvScale s;
+  s.g = g;
+  s.fast = g >= 0x1p-125f && g <= 0x1p100f;
+  s.k = kRcp6 * (1.0f / (s.fast ? g : 1.0f));
+  return s;
+}
+
+// The defining computation: E4M3 of fp32(fp32(amax / 6) / g), RNE, overflow
+// (0x7F) stepped down to 448. amag: FP32 bits of the block's largest magnitude
+// (>= 0x7F800000: NaN or Inf present).
+__device__ __forceinline__ uint32_t nv_code_exact(uint32_t amag, float g) {
+  if (amag >= 0x7F800000u) return 0x7Fu;
+  if (g == 0.0f) return 0u;
   const float t = (__uint_as_float(amag) / kE2m1Max) / g;
-  // E4M3 of t >= 0 (RNE); overflow (0x7F) steps down to 448
-  const uint32_t c = fix_overflow<kE4M3>(cvt2_f32<kE4M3, false>(0u, t, 0.0f, one)) & 0xFFu;
-  const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, one, false)[0];
-  b.code = c;
-  b.rcp = 1.0f / (s * g);
-  b.zero = c == 0u || !(__builtin_fabsf(b.rcp) < __builtin_inff());
+  return fix_overflow<kE4M3>(cvt2_f32<kE4M3, false>(0u, t, 0.0f, scale_operand(127u))) & 0xFFu;
+}
+
+// The same code through the estimate, falling back to nv_code_exact.
+__device__ __forceinline__ uint32_t nv_code(uint32_t amag, const NvScale& s) {
+  const uint32_t tb = min(__float_as_uint(__uint_as_float(amag) * s.k), kNvTcap);
+  const uint32_t lo = tb > kNvWindow ? tb - kNvWindow : 0u;
+  const uint32_t w = cvt2_f32<kE4M3, false>(0u, __uint_as_float(lo), __uint_as_float(tb + kNvWindow),
+                                            scale_operand(127u));
+  const uint32_t c0 = min(w & 0xFFu, 0x7Eu), c1 = min((w >> 8) & 0xFFu, 0x7Eu);
+  uint32_t c = c0;
+  bool slow = !(s.fast && amag >= kNvAmin && c0 == c1);
+  if (amag == 0u && s.fast) { c = 0u; slow = false; }
+  if (amag >= 0x7F800000u) { c = 0x7Fu; slow = false; }
+  if (slow) c = nv_code_exact(amag, s.g);
+  return c;
+}
+
+// LDS table of 1 / fp32(s_c * g) for every scale byte c; NaN marks the codes
+// whose blocks store codes 0 (c == 0, or the reciprocal is not finite).
+constexpr int kNvTab = 256;
+__device__ __forceinline__ void nv_fill_table(float* tab, float g) {
+  const int c = threadIdx.x;
+  if (c < kNvTab) {
+    const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uint32_t(c), scale_operand(127u), false)[0];
+    const float r = 1.0f / (s * g);
+    tab[c] = (c == 0 || !(__builtin_fabsf(r) < __builtin_inff())) ? __builtin_nanf("") : r;
+  }
+}
+
+__device__ __forceinline__ NvBlock nv_block(uint32_t amag, const NvScale& s, const float* tab) {
+  NvBlock b;
+  b.code = nv_code(amag, s);
+  b.rcp = tab[b.code];
+  b.zero = b.rcp != b.rcp;
   return b;
 }
 
@@ -138,6 +191,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
   __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * SPC : 4];
+  __shared__ float lds_rtab[kNvTab];
 
   uint32_t bi, tr, tcol;
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, bi, tr, tcol);
@@ -167,6 +221,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     const uint4 d = load_nt(xt + (ok ? xoff + uint32_t(k) * Cu * ES : 0u));
     v[k] = ok ? d : make_uint4(0u, 0u, 0u, 0u);
   }
+  const NvScale sc = nv_scale(g);
+  nv_fill_table(lds_rtab, g);
+  __syncthreads();
+
   // element e (0 .. VEC-1) of row k as FP32
   auto elem = [&](int k, int e) -> float {
     if constexpr (BF16) {
@@ -192,8 +250,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         cm[d] = pk_max_xor16(cm[d]);                     // row groups q and q ^ 1
-        cb[2 * d] = nv_block((cm[d] & 0xFFFFu) << 16, g);
-        cb[2 * d + 1] = nv_block(cm[d] & 0xFFFF0000u, g);
+        cb[2 * d] = nv_block((cm[d] & 0xFFFFu) << 16, sc, lds_rtab);
+        cb[2 * d + 1] = nv_block(cm[d] & 0xFFFF0000u, sc, lds_rtab);
       }
     } else {
 #pragma unroll
@@ -201,7 +259,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         uint32_t m = (&v[0].x)[d] & 0x7FFFFFFFu;
 #pragma unroll
         for (int k = 1; k < RPT; ++k) m = max(m, (&v[k].x)[d] & 0x7FFFFFFFu);
-        cb[d] = nv_block(m, g);
+        cb[d] = nv_block(m, sc, lds_rtab);
       }
     }
   }
@@ -225,7 +283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         m = max(max(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu), max(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu));
         m = group_max<4>(m);
       }
-      const NvBlock blk = nv_block(m, g);
+      const NvBlock blk = nv_block(m, sc, lds_rtab);
       const bool ok = col_ok && lrow + k < rows_in;
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu / 2;
       if constexpr (BF16) {

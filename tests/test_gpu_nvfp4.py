@@ -136,3 +136,58 @@ def test_full_activations(mx):
         assert np.array_equal(out["row_scales"][r0:r0 + 256].cpu().numpy(), exp["row_scales"])
         assert np.array_equal(out["col_codes"][:, r0 // 2:(r0 + 256) // 2].cpu().numpy(), exp["col_codes"])
         assert np.array_equal(out["col_scales"][:, r0 // 16:(r0 + 256) // 16].cpu().numpy(), exp["col_scales"])
+
+
+def _midpoint_blocks(A, seed):
+    """FP32 [R][256]: one element of magnitude A (so the tensor's global scale is
+    fp32(A / 2688)); every other 16-element block has its max within +-20 ulps
+    of a value whose scaled t sits on an E4M3 value or rounding midpoint."""
+    rng = np.random.default_rng(seed)
+    g = np.float32(A) / np.float32(2688)
+    vals = O.value_table(O.E4M3)[:127]
+    targets = np.concatenate([(vals[:-1] + vals[1:]) / 2, vals[1:], [464.0]])
+    n = len(targets) * 41
+    a = (np.repeat(targets, 41) * 6.0 * np.float64(g)).astype(np.float32)
+    a = (a.view(np.int32) + np.tile(np.arange(-20, 21, dtype=np.int32), len(targets))).view(np.float32)
+    a = np.minimum(a, np.float32(A))
+    blocks = (rng.random((n, 16)) * 0.9).astype(np.float32) * a[:, None]
+    blocks[np.arange(n), rng.integers(0, 16, n)] = a * np.where(rng.random(n) < 0.5, -1, 1).astype(np.float32)
+    blocks = np.concatenate([blocks, np.full((1, 16), A, np.float32)])
+    pad = (-len(blocks)) % 16
+    blocks = np.concatenate([blocks, np.zeros((pad, 16), np.float32)])
+    return torch.from_numpy(blocks.reshape(-1, 256))
+
+
+@pytest.mark.parametrize("A", [1000.0, 2688.0, 3.0e-30, 2.0 ** -110, 1.5e30])
+def test_block_codes_near_midpoints(mx, A):
+    """Block maxima next to every UE4M3 rounding boundary: the fast block-code
+    estimate must fall back wherever it cannot decide, and agree elsewhere."""
+    x = _midpoint_blocks(A, seed=67)
+    check(mx, x, "row", "mid/row")
+    xr = x[: (x.shape[0] // 16) * 16]
+    check(mx, xr.T.contiguous(), "both", "mid/both")
+
+
+def test_tiny_fp32_blocks(mx):
+    """FP32 blocks below 2^-120 under a normal global scale: their scaled maxima
+    still reach UE4M3 subnormals, and they take the exact two-division path."""
+    rng = np.random.default_rng(69)
+    e = rng.uniform(-149, -117, (64, 16, 1))
+    x = (rng.standard_normal((64, 16, 16)) * np.exp2(e)).astype(np.float32).reshape(64, 256)
+    x[0, 0] = np.float32(2.0 ** -110)
+    check(mx, torch.from_numpy(x), "both", "tiny")
+
+
+@pytest.mark.parametrize("gval", [0.0, 1e-38, 2.0 ** -125, 2.0 ** -126, 3.3e-30, 0.0371, 2.0 ** 100, 2.0 ** 101, 1e37])
+def test_given_global_scale_extremes(mx, gval):
+    """Caller-given global scales inside and outside the range where the block
+    code is estimated, over blocks spanning many binades."""
+    rng = np.random.default_rng(68)
+    e = rng.integers(-149, 128, (96, 1)).astype(np.float64)
+    x = (rng.standard_normal((96, 256)) * np.exp2(np.clip(e, -149, 126))).astype(np.float32)
+    x = torch.from_numpy(x)
+    gs = torch.tensor([gval], dtype=torch.float32)
+    out = mx.mx_quantize_nvfp4(x.cuda(), "both", global_scale=gs.cuda())
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    same(got, oracle(x, "both", gs.numpy()), f"given {gval}")
