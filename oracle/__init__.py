@@ -11,5 +11,7 @@ from .mx_variants import *  # noqa: F401,F403
 from .mx_variants import __all__ as _variant_all
 from .nvfp4 import *  # noqa: F401,F403
 from .nvfp4 import __all__ as _nv_all
+from .nested import *  # noqa: F401,F403
+from .nested import __all__ as _nested_all
 
-__all__ = list(_base_all) + list(_variant_all) + list(_nv_all)
+__all__ = list(_base_all) + list(_variant_all) + list(_nv_all) + list(_nested_all)

@@ -321,3 +321,44 @@ def test_pins_catch_nvfp4_elements_scaled_without_global():
     with planted_nv("_quant_plane", no_global):
         assert any_pin_fails([(PN.test_block_holding_the_tensor_max_decodes_exactly, ()),
                               (PN.test_scale_steps_match_torch_float32, ())])
+
+
+import oracle.nested as NS  # noqa: E402
+import test_oracle_nested as PNS  # noqa: E402
+
+NESTED_PINS = [(PNS.test_512_subtiles_per_block, ()), (PNS.test_lossless_below_threshold, (14,)),
+               (PNS.test_spread_15_loses_exactly_the_predicted_elements, ()),
+               (PNS.test_block_scale_places_the_largest_value_at_384, ()),
+               (PNS.test_zero_and_nan_subblocks_do_not_count, ()), (PNS.test_ragged_blocks_and_transpose, ()),
+               (PNS.test_pipeline_from_fp32_weights, ())]
+
+
+@contextlib.contextmanager
+def planted_nested(name, value):
+    old = getattr(NS, name)
+    setattr(NS, name, value)
+    try:
+        yield
+    finally:
+        setattr(NS, name, old)
+
+
+@pytest.mark.parametrize("shift", [5, 7])
+def test_pins_catch_nested_block_scale_off_by_one(shift):
+    with planted_nested("SHIFT", shift):
+        assert any_pin_fails(NESTED_PINS)
+
+
+def test_pins_catch_nested_zero_subblocks_counted():
+    with planted_nested("_active", lambda qs, k: k != M.E8M0_NAN):
+        assert any_pin_fails(NESTED_PINS)
+
+
+def test_pins_catch_nested_nan_subblocks_counted():
+    with planted_nested("_active", lambda qs, k: ((qs & 0x7) != 0).any(axis=-1)):
+        assert any_pin_fails(NESTED_PINS)
+
+
+def test_pins_catch_nested_64_blocks():
+    with planted_nested("FP8_BLOCK", 64):
+        assert any_pin_fails(NESTED_PINS)
