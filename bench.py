@@ -221,6 +221,34 @@ def _nvfp4_workload():
                        "input_reads": 2}}
 
 
+def _requant_workload():
+    """14336x4096 weights as MXFP4 (E2M1, floor, rows; made once, untimed) ->
+    FP8 E4M3 with 128x128 block scales, both the row copy and the transposed
+    copy, plus the per-block spread."""
+    r, c = 14336, 4096
+    n = r * c
+    nblk = (r // 128) * (c // 128)
+    nbytes = (n // 2 + n // 32) + 2 * (n + 4 * nblk) + nblk
+
+    def make(dev, i):
+        import torch
+        import microscaling_block_quantized_amd as mx
+        import mx_inputs as I
+        w = I.weights(r, c, seed=2 + 100 * i, device=dev)
+        q = mx.mx_quantize(w, "e2m1", "floor", "row")
+        del w
+        out = {"e4m3": torch.empty((r, c), dtype=torch.uint8, device=dev),
+               "block_scale": torch.empty((r // 128, c // 128), dtype=torch.float32, device=dev),
+               "e4m3_t": torch.empty((c, r), dtype=torch.uint8, device=dev),
+               "block_scale_t": torch.empty((c // 128, r // 128), dtype=torch.float32, device=dev),
+               "spread": torch.empty((r // 128, c // 128), dtype=torch.uint8, device=dev)}
+        return mx.BoundRequant(q["row_codes"], q["row_scales"], (r, c), "both", out)
+    desc = ("weights 14336x4096 as MXFP4 (E2M1 1x32, floor) -> FP8 E4M3 with 128x128 power-of-two block scales, "
+            "row copy + transposed copy + scale-spread check")
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+            "config": {"workload": desc, "rows": r, "cols": c, "fmt": "e2m1->e4m3", "axis": "both"}}
+
+
 def _wide_range_pipeline():
     """64 x 4096x14336 BF16: fused E4M3 quantize, then both planes dequantized to BF16."""
     b, r, c = 64, 4096, 14336
@@ -312,6 +340,7 @@ WORKLOADS = {
                                       "weights 14336x4096 bf16 -> MXFP4 E2M1 32x32 blocks, row+col fused, "
                                       "floor scale rule", block="32x32"),
     "act_nvfp4": _nvfp4_workload(),
+    "weights_fp4_in_fp8": _requant_workload(),
     "wide_range": _wide_range_pipeline(),
     "fp32_normal": _fp32_normal_round_trip(),
 }

@@ -174,7 +174,9 @@ int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_sh
  * NaN) and codes 0.
  *   global_scale  [batch] FP32, device memory: written (global_given == 0)
  *                 or read (global_given == 1, e.g. a scale kept from an
- *                 earlier step)
+ *                 earlier step). When written, it holds intermediate values
+ *                 (each slice's raw maximum with the sign bit set) until the
+ *                 stream has run the whole call, and g afterwards.
  *   row_codes     [batch][rows][cols/2] (element 2k in bits 3:0)
  *   row_scales    [batch][rows][cols/16] UE4M3 bytes
  *   col_codes     [batch][cols][rows/2]  (the same cast of X^T)
@@ -192,6 +194,33 @@ int mx_quantize_nvfp4(const void* x, mx_dtype x_dtype, mx_shape s, mx_axis axis,
  * gives the canonical NaN. codes 8-byte aligned, y 16-byte aligned. */
 int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* global_scale, mx_shape s,
                         mx_dtype y_dtype, void* y, void* stream);
+
+/* FP4-in-FP8 nested requantization (same article, §6, DeepSeek-V4's nested
+ * structure): an MXFP4 plane (E2M1 codes two per byte, one E8M0 scale per 32
+ * elements along cols, as mx_quantize writes it) re-expressed as FP8 E4M3
+ * with one FP32 scale per 128x128 block, which holds 512 of the 1x32
+ * sub-blocks. A sub-block is active when one of its codes has a nonzero
+ * magnitude and its scale is not 0xFF; kmax / kmin are the largest and
+ * smallest scale codes of a block's active sub-blocks. The block scale is
+ * S = 2^(kmax - 133) (1.0 for a block without active sub-blocks), so E2M1's 6
+ * at kmax lands on 384; element e2m1 * 2^(k - 127) is stored as the E4M3 code
+ * of its value / S, rounded to nearest-even, 0x7F in a NaN sub-block, zeros
+ * keeping their sign. spread = kmax - kmin (0 with fewer than two active
+ * sub-blocks) is the check the article asks for: spread <= 14 (a scale ratio
+ * of at most 2^14) makes every value / S an E4M3 value, so the block converts
+ * exactly; above that, the smallest sub-blocks can lose their 0.5 and 1.5.
+ * Blocks at a ragged edge cover the rows and columns present.
+ *   codes          [batch][rows][cols/2], 16-byte aligned; scales [batch][rows][cols/32]
+ *   fp8            [batch][rows][cols] E4M3, 16-byte aligned  (MX_AXIS_ROW)
+ *   block_scale    [batch][R'][C'] FP32, R' = ceil(rows/128), C' = ceil(cols/128)
+ *   fp8_t          [batch][cols][rows]: the same codes transposed (MX_AXIS_COL;
+ *                  the square blocks make the transposed weight need no new
+ *                  quantization), 16-byte aligned, rows % 16 == 0
+ *   block_scale_t  [batch][C'][R'] FP32 (the transposed grid)
+ *   spread         [batch][R'][C'] bytes, or NULL
+ * Shape: cols % 32 == 0. Pointers of an axis not requested must be NULL. */
+int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_axis axis, uint8_t* fp8,
+                       float* block_scale, uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream);
 
 /* Static text for an MX_* code; never NULL. */
 const char* mx_strerror(int err);

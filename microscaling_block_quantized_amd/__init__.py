@@ -23,8 +23,8 @@ import os
 
 __all__ = [
     "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "ROUNDING", "BLOCK", "MxQuantOpts", "lib_path", "load", "mx_version", "mx_strerror",
-    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "EXPORTS",
-    "BoundQuantize", "BoundDequantize", "BoundQuantizeNvfp4",
+    "mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_quantize_nvfp4", "mx_dequantize_nvfp4",
+    "mx_requant_fp4_fp8", "EXPORTS", "BoundQuantize", "BoundDequantize", "BoundQuantizeNvfp4", "BoundRequant",
 ]
 
 FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4, "int8": 5}
@@ -35,7 +35,7 @@ ROUNDING = {"rne": 0, "sr": 1}
 BLOCK = {"1x32": 0, "32x32": 1}
 DTYPE = {"f32": 0, "bf16": 1}
 EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_quantize_ex", "mx_dequantize", "mx_dequantize_ex",
-           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_strerror", "mx_version")
+           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_requant_fp4_fp8", "mx_strerror", "mx_version")
 
 _LIB = None
 
@@ -89,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.mx_quantize_nvfp4.argtypes = [vp, i32, MxShape, i32, vp, i32, vp, u8p, vp, u8p, vp]
     lib.mx_dequantize_nvfp4.restype = i32
     lib.mx_dequantize_nvfp4.argtypes = [vp, u8p, vp, MxShape, i32, vp, vp]
+    lib.mx_requant_fp4_fp8.restype = i32
+    lib.mx_requant_fp4_fp8.argtypes = [vp, u8p, MxShape, i32, u8p, vp, u8p, vp, u8p, vp]
     _LIB = lib
     return lib
 
@@ -344,3 +346,63 @@ class BoundQuantizeNvfp4:
         err = self._fn(*self._args)
         if err:
             raise MXError(err, "mx_quantize_nvfp4")
+
+
+def _rq_planes(codes, shape, axis: str, spread: bool, out: dict | None):
+    import torch
+    b, r, c = _shape3(shape)
+    nbr, nbc = -(-r // 128), -(-c // 128)
+    dev = codes.device
+    out = dict(out or {})
+    lead = (b,) if len(shape) == 3 else ()
+    if AXIS[axis] & 1:
+        out.setdefault("e4m3", torch.empty(lead + (r, c), dtype=torch.uint8, device=dev))
+        out.setdefault("block_scale", torch.empty(lead + (nbr, nbc), dtype=torch.float32, device=dev))
+    if AXIS[axis] & 2:
+        out.setdefault("e4m3_t", torch.empty(lead + (c, r), dtype=torch.uint8, device=dev))
+        out.setdefault("block_scale_t", torch.empty(lead + (nbc, nbr), dtype=torch.float32, device=dev))
+    if spread:
+        out.setdefault("spread", torch.empty(lead + (nbr, nbc), dtype=torch.uint8, device=dev))
+    return out
+
+
+def mx_requant_fp4_fp8(codes, scales, shape, axis: str = "row", spread: bool = True, out: dict | None = None):
+    """FP4-in-FP8 requantization of an MXFP4 plane (codes [..][R][C/2], scales
+    [..][R][C/32] as mx_quantize writes them; ``shape`` is its element shape
+    [R][C] or [B][R][C]).
+
+    Returns {"e4m3" [..][R][C], "block_scale" [..][R'][C'] float32} for the row
+    axis, {"e4m3_t" [..][C][R], "block_scale_t" [..][C'][R']} for the column axis,
+    and "spread" [..][R'][C'] (largest minus smallest active scale code of each
+    128x128 block; the block converted exactly when it is at most 14).
+    """
+    if not codes.is_cuda or not scales.is_cuda:
+        raise ValueError("mx_requant_fp4_fp8 needs GPU tensors (libmx has no CPU path)")
+    import torch
+    b, r, c = _shape3(shape)
+    planes = _rq_planes(codes, shape, axis, spread, out)
+    with torch.cuda.device(codes.device):
+        err = load().mx_requant_fp4_fp8(
+            _ptr(codes), _ptr(scales), MxShape(b, r, c), AXIS[axis], _ptr(planes.get("e4m3")),
+            _ptr(planes.get("block_scale")), _ptr(planes.get("e4m3_t")), _ptr(planes.get("block_scale_t")),
+            _ptr(planes.get("spread")), _stream_of(codes))
+    if err:
+        raise MXError(err, "mx_requant_fp4_fp8")
+    return planes
+
+
+class BoundRequant:
+    """An mx_requant_fp4_fp8 call marshalled once (see BoundQuantize)."""
+
+    def __init__(self, codes, scales, shape, axis: str, out: dict):
+        b, r, c = _shape3(shape)
+        self._fn = load().mx_requant_fp4_fp8
+        self._args = (_ptr(codes), _ptr(scales), MxShape(b, r, c), AXIS[axis], _ptr(out.get("e4m3")),
+                      _ptr(out.get("block_scale")), _ptr(out.get("e4m3_t")), _ptr(out.get("block_scale_t")),
+                      _ptr(out.get("spread")), _stream_of(codes))
+        self._keep = (codes, scales, out)
+
+    def __call__(self) -> None:
+        err = self._fn(*self._args)
+        if err:
+            raise MXError(err, "mx_requant_fp4_fp8")

@@ -55,7 +55,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10300; }
+int mx_version(void) { return 10400; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -225,6 +225,7 @@ int mx_quantize_nvfp4(const void* x, mx_dtype x_dtype, mx_shape s, mx_axis axis,
   if (!global_given) {
     const hipError_t e = mx::launch_nvfp4_global(bf, x, s.batch, s.rows * s.cols, global_scale, st);
     if (e != hipSuccess) return MX_ERR_LAUNCH;
+    a.flags |= mx::kNvMarkedAmax;
   }
   const hipError_t e = mx::launch_nvfp4_cast(bf, int(axis), a, uint32_t(g.blocks), st);
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
@@ -246,6 +247,52 @@ int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* g
   const hipError_t e = mx::launch_nvfp4_dequant(y_dtype == MX_BF16, static_cast<const uint8_t*>(codes), scales,
                                                 global_scale, y, n / kNv, s.rows * s.cols / kNv,
                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_axis axis, uint8_t* fp8,
+                       float* block_scale, uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream) {
+  if (!valid_axis(axis)) return MX_ERR_ENUM;
+  const bool want_row = (axis & MX_AXIS_ROW) != 0;
+  const bool want_col = (axis & MX_AXIS_COL) != 0;
+  if (codes == nullptr || scales == nullptr) return MX_ERR_NULL;
+  if (want_row != (fp8 != nullptr) || want_row != (block_scale != nullptr)) return MX_ERR_NULL;
+  if (want_col != (fp8_t != nullptr) || want_col != (block_scale_t != nullptr)) return MX_ERR_NULL;
+  const int64_t n = elements(s);
+  if (n < 0 || s.cols % kBlock != 0 || (want_col && s.rows % 16 != 0)) return MX_ERR_SHAPE;
+  if (!aligned(codes, 16) || (want_row && (!aligned(fp8, 16) || !aligned(block_scale, 4))) ||
+      (want_col && (!aligned(fp8_t, 16) || !aligned(block_scale_t, 4))))
+    return MX_ERR_ALIGN;
+  const int64_t nbr = (s.rows + 127) / 128, nbc = (s.cols + 127) / 128;
+  const int64_t nblk = s.batch * nbr * nbc;
+  Range rs[7];
+  int nr = 0;
+  rs[nr++] = range_of(codes, n / 2);
+  rs[nr++] = range_of(scales, n / kBlock);
+  if (want_row) { rs[nr++] = range_of(fp8, n); rs[nr++] = range_of(block_scale, nblk * 4); }
+  if (want_col) { rs[nr++] = range_of(fp8_t, n); rs[nr++] = range_of(block_scale_t, nblk * 4); }
+  if (spread != nullptr) rs[nr++] = range_of(spread, nblk);
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
+  if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;
+  const int64_t tiles_r = nbr, tiles_c = (s.cols + 255) / 256;
+  const int64_t blocks = s.batch * tiles_r * tiles_c;
+  if (blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
+
+  mx::RqArgs a;
+  a.codes = static_cast<const uint8_t*>(codes);
+  a.scales = scales;
+  a.fp8 = fp8;
+  a.block_scale = block_scale;
+  a.fp8_t = fp8_t;
+  a.block_scale_t = block_scale_t;
+  a.spread = spread;
+  a.rows = s.rows;
+  a.cols = s.cols;
+  a.tiles_r = uint32_t(tiles_r);
+  a.tiles_c = uint32_t(tiles_c);
+  const hipError_t e = mx::launch_requant(int(axis), a, uint32_t(blocks), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 

@@ -26,6 +26,7 @@ struct CastArgs {
 // With 32x32 blocks the pitches are C/32 (row copy) and R/32 (column copy).
 constexpr uint32_t kRowScaleDword = 1u;
 constexpr uint32_t kColScaleDword = 2u;
+constexpr uint32_t kNvMarkedAmax = 4u;   // NVFP4 cast: global_scale holds marked maxima
 
 struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;
@@ -52,18 +53,35 @@ struct NvArgs {
   uint8_t* row_scales;         // [batch][rows][cols/16] or null
   void* col_codes;             // [batch][cols][rows/2] or null
   uint8_t* col_scales;         // [batch][cols][rows/16] or null
-  const float* global_scale;   // [batch]
+  float* global_scale;         // [batch]; with kNvMarkedAmax, raw marked maxima that the cast turns into g
   int64_t rows, cols;
   uint32_t tiles_r, tiles_c;
   uint32_t flags;              // kRowScaleDword: cols % 64 == 0; kColScaleDword: rows % 64 == 0
 };
 
-// g[b] = (largest finite |x| of slice b) / 2688 into gs[0 .. batch-1] (three launches).
+// gs[b] = (largest finite |x| of slice b) as FP32 bits with the sign bit set
+// (two launches); the cast, given kNvMarkedAmax, turns it into g = amax / 2688.
 hipError_t launch_nvfp4_global(bool in_bf16, const void* x, int64_t batch, int64_t slice_elems, float* gs,
                                hipStream_t s);
 hipError_t launch_nvfp4_cast(bool in_bf16, int axis, const NvArgs& a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_nvfp4_dequant(bool out_bf16, const uint8_t* codes, const uint8_t* scales, const float* gs,
                                 void* y, int64_t nblocks, int64_t blocks_per_slice, hipStream_t s);
+
+// FP4-in-FP8 requantization of one MXFP4 plane [batch][rows][cols] (codes two per
+// byte, E8M0 scales per 32 elements along cols) into E4M3 with one FP32 scale
+// per 128x128 block (mx_requant.hip).
+struct RqArgs {
+  const uint8_t* codes;        // [batch][rows][cols/2]
+  const uint8_t* scales;       // [batch][rows][cols/32]
+  uint8_t* fp8;                // [batch][rows][cols] or null
+  float* block_scale;          // [batch][R'][C'] or null (R' = ceil(rows/128), C' = ceil(cols/128))
+  uint8_t* fp8_t;              // [batch][cols][rows] or null
+  float* block_scale_t;        // [batch][C'][R'] or null
+  uint8_t* spread;             // [batch][R'][C'] or null
+  int64_t rows, cols;
+  uint32_t tiles_r, tiles_c;   // 128-row x 256-column tiles per slice
+};
+hipError_t launch_requant(int axis, const RqArgs& a, uint32_t nblocks, hipStream_t s);
 
 // Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
 // or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale

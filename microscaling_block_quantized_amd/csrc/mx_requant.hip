@@ -1,0 +1,228 @@
+// FP4-in-FP8 nested requantization.
+//
+// "MXFP4 と NVFP4 は何が違うのか調べてみた" §6 (DeepSeek-V4's nested structure):
+// MXFP4 weights (1x32 tiles with E8M0 scales) are dequantized into FP8 E4M3
+// whose scales are per 128x128 tile, which holds 512 of the 1x32 tiles; the
+// conversion is lossless while, inside each 128x128 tile, the largest and the
+// smallest 1x32 scale stay within a bounded ratio, a property of the weights
+// that has to be checked. The arithmetic fixed here:
+//   * a 1x32 sub-block is active when one of its codes has a nonzero
+//     magnitude and its scale is not 0xFF; kmax / kmin are the largest and
+//     smallest scale codes of the block's active sub-blocks;
+//   * the block scale is S = 2^(kmax - 133), so E2M1's 6 of the largest
+//     sub-block lands on 384 (S = 1 for a block with no active sub-block);
+//   * element v = e2m1 * 2^(k - 127) is stored as E4M3(v / S), nearest-even;
+//     0x7F for a NaN sub-block;
+//   * spread = kmax - kmin (0 without two active sub-blocks); spread <= 14
+//     makes every v / S an E4M3 value, so the block converts exactly.
+// v / S = e2m1 * 2^(k - kmax + 6) is formed exactly by decoding the E2M1 codes
+// with the scale code k - kmax + 133 (clamped to [0, 254]: outside that range
+// the values are zeros, or tinier than half E4M3's smallest subnormal), then
+// encoded with scale 1: the gfx950 conversions are exact and round to
+// nearest-even.
+//
+// One workgroup of 4 waves owns a 128-row x 256-column tile: two FP8 blocks
+// side by side. Thread t reads rows 4q .. 4q+3 (q = t / 8) of sub-block column
+// t % 8, so 8 lanes read one 128-byte run of a row. The transposed copy is
+// staged as [column][row] bytes in LDS, each 16-byte chunk index XORed with
+// the column's sub-block, and written as 128-byte runs of the [C][R] plane.
+#include "mx_cast_impl.h"   // memory helpers (non-temporal loads and stores)
+#include "mx_kernels.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int kRqRows = 128;
+constexpr int kRqCols = 256;
+constexpr int kRqThreads = 256;
+constexpr int kRqWaves = kRqThreads / 64;
+constexpr uint32_t kRqShift = 133;            // 127 + 6
+
+// 4x4 byte transpose: byte j of result i is byte i of a[j].
+__device__ __forceinline__ void transpose4x4(const uint32_t* a, uint32_t* c) {
+  const uint32_t t0 = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+  c[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  c[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  c[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Max of two packed 16-bit fields over the whole wave.
+__device__ __forceinline__ uint32_t wave_pk_max(uint32_t v) {
+  v = pk_max_u16(v, dpp<kDppXor1>(v));
+  v = pk_max_u16(v, dpp<kDppXor2>(v));
+  v = pk_max_u16(v, dpp<kDppHalfMirror>(v));
+  v = pk_max_u16(v, dpp<kDppRor8>(v));
+  return pk_max_xor32(pk_max_xor16(v));
+}
+
+// 32 E2M1 codes (16 bytes) decoded with scale code c and re-encoded as E4M3.
+__device__ __forceinline__ void e2m1_to_e4m3(const uint4& w, uint32_t c, uint32_t* out) {
+  const float sc = scale_operand(c);
+  const float one = scale_operand(127u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t cw = (&w.x)[d];
+    float2v f0, f1, f2, f3;
+    f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 0);
+    f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 1);
+    f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 2);
+    f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 3);
+    uint32_t lo = cvt2_f32<kE4M3, false>(0u, f0[0], f0[1], one);
+    lo = cvt2_f32<kE4M3, true>(lo, f1[0], f1[1], one);
+    uint32_t hi = cvt2_f32<kE4M3, false>(0u, f2[0], f2[1], one);
+    hi = cvt2_f32<kE4M3, true>(hi, f3[0], f3[1], one);
+    out[2 * d] = lo;
+    out[2 * d + 1] = hi;
+  }
+}
+
+template <bool ROWS, bool COLS>
+__global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
+  __shared__ uint32_t part[kRqWaves][2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t[COLS ? kRqCols * kRqRows : 16];
+
+  const uint32_t per_slice = a.tiles_r * a.tiles_c;
+  const uint32_t bi = blockIdx.x / per_slice;
+  const uint32_t rem = blockIdx.x % per_slice;
+  const uint32_t tr = rem / a.tiles_c, tc = rem % a.tiles_c;
+  const int64_t R = a.rows, C = a.cols;
+  const int64_t r0 = int64_t(tr) * kRqRows, c0 = int64_t(tc) * kRqCols;
+  const int rows_in = int(min<int64_t>(R - r0, kRqRows));
+  const int cols_in = int(min<int64_t>(C - c0, kRqCols));
+  const uint32_t Cu = uint32_t(C);
+
+  const int t = threadIdx.x;
+  const int q = t >> 3, sb = t & 7, blk = sb >> 2;
+  const bool col_ok = 32 * sb < cols_in;
+
+  // ---- load 4 rows x 16 code bytes and their 4 scales ----
+  const int64_t tile_row = int64_t(bi) * R + r0;
+  const uint8_t* ct = a.codes + tile_row * (C / 2) + c0 / 2;
+  const uint8_t* st = a.scales + tile_row * (C / 32) + c0 / 32;
+  uint4 w[4];
+  uint32_t k[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * q + i;
+    const bool ok = col_ok && row < rows_in;
+    const uint4 d = load_nt(ct + (ok ? uint32_t(row) * (Cu / 2) + 16u * sb : 0u));
+    const uint32_t kk = st[ok ? uint32_t(row) * (Cu / 32) + sb : 0u];
+    w[i] = ok ? d : make_uint4(0u, 0u, 0u, 0u);
+    k[i] = ok ? kk : 0u;
+  }
+
+  // ---- kmax / kmin over active sub-blocks, per FP8 block (16-bit fields: k + 1, 256 - k) ----
+  uint32_t fmax = 0, fmin = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool act = k[i] != 0xFFu && ((w[i].x | w[i].y | w[i].z | w[i].w) & 0x77777777u) != 0u;
+    fmax = max(fmax, act ? k[i] + 1u : 0u);
+    fmin = max(fmin, act ? 256u - k[i] : 0u);
+  }
+  uint32_t pmax = wave_pk_max(blk ? fmax << 16 : fmax);
+  uint32_t pmin = wave_pk_max(blk ? fmin << 16 : fmin);
+  if ((t & 63) == 0) {
+    part[t >> 6][0] = pmax;
+    part[t >> 6][1] = pmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < kRqWaves; ++v) {
+    pmax = pk_max_u16(pmax, part[v][0]);
+    pmin = pk_max_u16(pmin, part[v][1]);
+  }
+  const uint32_t fa = blk ? pmax >> 16 : pmax & 0xFFFFu;
+  const uint32_t fb = blk ? pmin >> 16 : pmin & 0xFFFFu;
+  const int kmax = fa ? int(fa) - 1 : int(kRqShift);
+
+  // ---- block scales and spreads (threads 0 and 4: the two blocks' first sub-block columns) ----
+  if (q == 0 && (sb & 3) == 0 && col_ok) {
+    const int64_t nbr = (R + kRqRows - 1) / kRqRows, nbc = (C + 127) / 128;
+    const int64_t br = tr, bc = int64_t(2) * tc + blk;
+    // 2^(kmax - 133): normal for kmax >= 7, subnormal below
+    const uint32_t sbits = kmax >= 7 ? uint32_t(kmax - 6) << 23 : 1u << (kmax + 16);
+    if (ROWS) a.block_scale[(int64_t(bi) * nbr + br) * nbc + bc] = __uint_as_float(sbits);
+    if (COLS) a.block_scale_t[(int64_t(bi) * nbc + bc) * nbr + br] = __uint_as_float(sbits);
+    if (a.spread) a.spread[(int64_t(bi) * nbr + br) * nbc + bc] = uint8_t(fa ? kmax - (256 - int(fb)) : 0);
+  }
+
+  // ---- convert ----
+  uint32_t e[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int c = int(k[i]) - kmax + int(kRqShift);
+    c = c < 0 ? 0 : (c > 254 ? 254 : c);
+    e2m1_to_e4m3(w[i], uint32_t(c), e[i]);
+    if (k[i] == 0xFFu) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[i][j] = 0x7F7F7F7Fu;
+    }
+  }
+
+  if constexpr (ROWS) {
+    uint8_t* ot = a.fp8 + tile_row * C + c0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * q + i;
+      if (col_ok && row < rows_in) {
+        uint8_t* dst = ot + uint32_t(row) * Cu + 32u * sb;
+        store_nt16(dst, make_uint4(e[i][0], e[i][1], e[i][2], e[i][3]));
+        store_nt16(dst + 16, make_uint4(e[i][4], e[i][5], e[i][6], e[i][7]));
+      }
+    }
+  }
+
+  if constexpr (COLS) {
+    // column cl = 32 sb + j holds rows 4q .. 4q+3 in one dword
+    const int chunk = ((q >> 2) ^ sb) << 4;
+    const int within = (q & 3) << 2;
+    if (col_ok) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t rows4[4] = {e[0][m], e[1][m], e[2][m], e[3][m]};
+        uint32_t cols4[4];
+        transpose4x4(rows4, cols4);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int cl = 32 * sb + 4 * m + jj;
+          *reinterpret_cast<uint32_t*>(lds_t + cl * kRqRows + chunk + within) = cols4[jj];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t Ru = uint32_t(R);
+    uint8_t* ot = a.fp8_t + (int64_t(bi) * C + c0) * R + r0;
+#pragma unroll
+    for (int i = 0; i < kRqCols * (kRqRows / 16) / kRqThreads; ++i) {
+      const int id = t + i * kRqThreads;
+      const int cl = id >> 3, c16 = id & 7;
+      if (cl < cols_in && 16 * c16 < rows_in) {
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_t + cl * kRqRows + (((c16 ^ (cl >> 5)) & 7) << 4));
+        store_nt16(ot + uint32_t(cl) * Ru + 16u * c16, v);
+      }
+    }
+  }
+}
+
+template <bool ROWS, bool COLS>
+hipError_t launch_rq(const RqArgs& a, uint32_t nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((requant_kernel<ROWS, COLS>), dim3(nblocks), dim3(kRqThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_requant(int axis, const RqArgs& a, uint32_t nblocks, hipStream_t s) {
+  switch (axis) {
+    case kRow: return launch_rq<true, false>(a, nblocks, s);
+    case kCol: return launch_rq<false, true>(a, nblocks, s);
+    default: return launch_rq<true, true>(a, nblocks, s);
+  }
+}
+
+}  // namespace mx

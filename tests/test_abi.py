@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10300
+    assert mxb.mx_version() == 10400
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -193,3 +193,33 @@ def test_nvfp4_argument_errors(lib):
     assert nd(shape=(1, 64, 24)) == E_SHAPE
     assert nd(c=CC + 4) == E_ALIGN
     assert nd(y=CC + 16) == E_ALIAS
+
+
+def test_requant_argument_errors(lib):
+    """mx_requant_fp4_fp8: every case fails validation (addresses 4 GiB apart)."""
+    v = lambda p: ctypes.c_void_p(p)
+    G = 1 << 32
+    C_, S_, F_, B_, FT, BT, SP = (G * k for k in range(1, 8))
+
+    def rq(c=C_, s=S_, shape=(1, 64, 64), axis=3, f=F_, b=B_, ft=FT, bt=BT, sp=SP):
+        return lib.mx_requant_fp4_fp8(v(c), v(s), MxShape(*shape), axis, v(f), v(b), v(ft), v(bt), v(sp), None)
+    assert rq(axis=0) == E_ENUM
+    assert rq(axis=4) == E_ENUM
+    assert rq(c=0) == E_NULL
+    assert rq(s=0) == E_NULL
+    assert rq(f=0) == E_NULL                                     # row axis without its codes
+    assert rq(axis=1) == E_NULL                                  # column planes given without the column axis
+    assert rq(axis=2, bt=0) == E_NULL
+    assert rq(shape=(1, 64, 48)) == E_SHAPE                      # cols % 32
+    assert rq(shape=(0, 64, 64)) == E_SHAPE
+    assert rq(shape=(1, 40, 64)) == E_SHAPE                      # rows % 16 with the transposed copy
+    # the row copy alone accepts 40 rows: the alias check after it fails
+    assert rq(shape=(1, 40, 64), axis=1, ft=0, bt=0, f=C_ + 16) == E_ALIAS
+    assert rq(c=C_ + 8) == E_ALIGN
+    assert rq(f=F_ + 8) == E_ALIGN
+    assert rq(ft=FT + 8) == E_ALIGN
+    assert rq(b=B_ + 2) == E_ALIGN
+    assert rq(sp=C_ + 4) == E_ALIAS                              # spread overlaps the codes
+    assert rq(bt=F_ + 16) == E_ALIAS
+    assert rq(shape=(1, 1, 1 << 22), axis=1, ft=0, bt=0) == E_BIG
+    assert rq(shape=(1, 1 << 23, 32)) == E_BIG                   # transposed rows too long
