@@ -278,7 +278,7 @@ int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_
   if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;
   const int64_t tiles_r = nbr, tiles_c = (s.cols + 255) / 256;
   const int64_t blocks = s.batch * tiles_r * tiles_c;
-  if (blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
+  if (blocks > UINT32_MAX / 2) return MX_ERR_TOO_LARGE;
 
   mx::RqArgs a;
   a.codes = static_cast<const uint8_t*>(codes);
@@ -292,7 +292,8 @@ int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_
   a.cols = s.cols;
   a.tiles_r = uint32_t(tiles_r);
   a.tiles_c = uint32_t(tiles_c);
-  const hipError_t e = mx::launch_requant(int(axis), a, uint32_t(blocks), static_cast<hipStream_t>(stream));
+  a.total_tiles = uint32_t(blocks);
+  const hipError_t e = mx::launch_requant(int(axis), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 

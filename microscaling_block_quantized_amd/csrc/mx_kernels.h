@@ -80,8 +80,9 @@ struct RqArgs {
   uint8_t* spread;             // [batch][R'][C'] or null
   int64_t rows, cols;
   uint32_t tiles_r, tiles_c;   // 128-row x 256-column tiles per slice
+  uint32_t total_tiles;        // batch * tiles_r * tiles_c: one workgroup each
 };
-hipError_t launch_requant(int axis, const RqArgs& a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_requant(int axis, const RqArgs& a, hipStream_t s);
 
 // Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
 // or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale

@@ -22,10 +22,13 @@
 // nearest-even.
 //
 // One workgroup of 4 waves owns a 128-row x 256-column tile: two FP8 blocks
-// side by side. Thread t reads rows 4q .. 4q+3 (q = t / 8) of sub-block column
-// t % 8, so 8 lanes read one 128-byte run of a row. The transposed copy is
-// staged as [column][row] bytes in LDS, each 16-byte chunk index XORed with
-// the column's sub-block, and written as 128-byte runs of the [C][R] plane.
+// side by side. Thread t = 16 g + h holds rows 8g .. 8g+7 of half sub-block h
+// (16 codes: 8 bytes in, 16 bytes out), so 16 lanes cover a row and every
+// load and store instruction moves whole 128-byte lines (4 rows of 128 bytes
+// in, 4 rows of 256 bytes out). The transposed copy is staged as
+// [column][row] bytes in LDS: each thread's 8 rows of a column are one 8-byte
+// slot, slot g of column c stored at slot g ^ (c / 16) (conflict-free for a
+// quarter wave), and leaves as 128-byte runs of the [C][R] plane.
 #include "mx_cast_impl.h"   // memory helpers (non-temporal loads and stores)
 #include "mx_kernels.h"
 
@@ -38,6 +41,7 @@ constexpr int kRqCols = 256;
 constexpr int kRqThreads = 256;
 constexpr int kRqWaves = kRqThreads / 64;
 constexpr uint32_t kRqShift = 133;            // 127 + 6
+constexpr int kRqRowsPerThread = 8;
 
 // 4x4 byte transpose: byte j of result i is byte i of a[j].
 __device__ __forceinline__ void transpose4x4(const uint32_t* a, uint32_t* c) {
@@ -60,18 +64,17 @@ __device__ __forceinline__ uint32_t wave_pk_max(uint32_t v) {
   return pk_max_xor32(pk_max_xor16(v));
 }
 
-// 32 E2M1 codes (16 bytes) decoded with scale code c and re-encoded as E4M3.
-__device__ __forceinline__ void e2m1_to_e4m3(const uint4& w, uint32_t c, uint32_t* out) {
+// 16 E2M1 codes (8 bytes) decoded with scale code c and re-encoded as E4M3 (16 bytes).
+__device__ __forceinline__ void e2m1x16_to_e4m3(const uint2& w, uint32_t c, uint32_t* out) {
   const float sc = scale_operand(c);
   const float one = scale_operand(127u);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t cw = (&w.x)[d];
-    float2v f0, f1, f2, f3;
-    f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 0);
-    f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 1);
-    f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 2);
-    f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 3);
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t cw = d ? w.y : w.x;
+    const float2v f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 0);
+    const float2v f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 1);
+    const float2v f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 2);
+    const float2v f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 3);
     uint32_t lo = cvt2_f32<kE4M3, false>(0u, f0[0], f0[1], one);
     lo = cvt2_f32<kE4M3, true>(lo, f1[0], f1[1], one);
     uint32_t hi = cvt2_f32<kE4M3, false>(0u, f2[0], f2[1], one);
@@ -97,30 +100,36 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
   const uint32_t Cu = uint32_t(C);
 
   const int t = threadIdx.x;
-  const int q = t >> 3, sb = t & 7, blk = sb >> 2;
-  const bool col_ok = 32 * sb < cols_in;
+  const int g = t >> 4, h = t & 15;
+  const int sbk = h >> 1, blk = h >> 3;          // sub-block of the tile row, FP8 block
+  const bool col_ok = 32 * sbk < cols_in;
 
-  // ---- load 4 rows x 16 code bytes and their 4 scales ----
+  // ---- load 8 rows x 8 code bytes and their scales ----
   const int64_t tile_row = int64_t(bi) * R + r0;
-  const uint8_t* ct = a.codes + tile_row * (C / 2) + c0 / 2;
-  const uint8_t* st = a.scales + tile_row * (C / 32) + c0 / 32;
-  uint4 w[4];
-  uint32_t k[4];
+  const uint8_t* ct = a.codes + tile_row * (C / 2) + c0 / 2 + 8 * h;
+  const uint8_t* st = a.scales + tile_row * (C / 32) + c0 / 32 + sbk;
+  uint2 w[kRqRowsPerThread];
+  uint32_t k[kRqRowsPerThread];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * q + i;
+  for (int i = 0; i < kRqRowsPerThread; ++i) {
+    const int row = kRqRowsPerThread * g + i;
     const bool ok = col_ok && row < rows_in;
-    const uint4 d = load_nt(ct + (ok ? uint32_t(row) * (Cu / 2) + 16u * sb : 0u));
-    const uint32_t kk = st[ok ? uint32_t(row) * (Cu / 32) + sb : 0u];
-    w[i] = ok ? d : make_uint4(0u, 0u, 0u, 0u);
+    const u32x2 d = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x2*>(ct + (ok ? uint32_t(row) * (Cu / 2) : 0u)));
+    const uint32_t kk = st[ok ? uint32_t(row) * (Cu / 32) : 0u];
+    w[i] = ok ? make_uint2(d.x, d.y) : make_uint2(0u, 0u);
     k[i] = ok ? kk : 0u;
   }
 
   // ---- kmax / kmin over active sub-blocks, per FP8 block (16-bit fields: k + 1, 256 - k) ----
+  uint32_t nz = 0;                               // bit i: row i's half has a nonzero magnitude
+#pragma unroll
+  for (int i = 0; i < kRqRowsPerThread; ++i) nz |= (((w[i].x | w[i].y) & 0x77777777u) != 0u) ? 1u << i : 0u;
+  nz |= dpp<kDppXor1>(nz);                       // the other half of the sub-block (lane h ^ 1)
   uint32_t fmax = 0, fmin = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool act = k[i] != 0xFFu && ((w[i].x | w[i].y | w[i].z | w[i].w) & 0x77777777u) != 0u;
+  for (int i = 0; i < kRqRowsPerThread; ++i) {
+    const bool act = k[i] != 0xFFu && ((nz >> i) & 1u);
     fmax = max(fmax, act ? k[i] + 1u : 0u);
     fmin = max(fmin, act ? 256u - k[i] : 0u);
   }
@@ -140,8 +149,8 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
   const uint32_t fb = blk ? pmin >> 16 : pmin & 0xFFFFu;
   const int kmax = fa ? int(fa) - 1 : int(kRqShift);
 
-  // ---- block scales and spreads (threads 0 and 4: the two blocks' first sub-block columns) ----
-  if (q == 0 && (sb & 3) == 0 && col_ok) {
+  // ---- block scales and spreads (threads 0 and 8: the two blocks' first half sub-blocks) ----
+  if (g == 0 && (h & 7) == 0 && col_ok) {
     const int64_t nbr = (R + kRqRows - 1) / kRqRows, nbc = (C + 127) / 128;
     const int64_t br = tr, bc = int64_t(2) * tc + blk;
     // 2^(kmax - 133): normal for kmax >= 7, subnormal below
@@ -151,46 +160,41 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
     if (a.spread) a.spread[(int64_t(bi) * nbr + br) * nbc + bc] = uint8_t(fa ? kmax - (256 - int(fb)) : 0);
   }
 
-  // ---- convert ----
-  uint32_t e[4][8];
+  // ---- convert: 16 codes per row -> 16 E4M3 bytes ----
+  uint32_t e[kRqRowsPerThread][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kRqRowsPerThread; ++i) {
     int c = int(k[i]) - kmax + int(kRqShift);
     c = c < 0 ? 0 : (c > 254 ? 254 : c);
-    e2m1_to_e4m3(w[i], uint32_t(c), e[i]);
-    if (k[i] == 0xFFu) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[i][j] = 0x7F7F7F7Fu;
-    }
+    e2m1x16_to_e4m3(w[i], uint32_t(c), e[i]);
+    if (k[i] == 0xFFu) e[i][0] = e[i][1] = e[i][2] = e[i][3] = 0x7F7F7F7Fu;
   }
 
   if constexpr (ROWS) {
-    uint8_t* ot = a.fp8 + tile_row * C + c0;
+    uint8_t* ot = a.fp8 + tile_row * C + c0 + 16 * h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * q + i;
-      if (col_ok && row < rows_in) {
-        uint8_t* dst = ot + uint32_t(row) * Cu + 32u * sb;
-        store_nt16(dst, make_uint4(e[i][0], e[i][1], e[i][2], e[i][3]));
-        store_nt16(dst + 16, make_uint4(e[i][4], e[i][5], e[i][6], e[i][7]));
-      }
+    for (int i = 0; i < kRqRowsPerThread; ++i) {
+      const int row = kRqRowsPerThread * g + i;
+      if (col_ok && row < rows_in)
+        store_nt16(ot + uint32_t(row) * Cu, make_uint4(e[i][0], e[i][1], e[i][2], e[i][3]));
     }
   }
 
   if constexpr (COLS) {
-    // column cl = 32 sb + j holds rows 4q .. 4q+3 in one dword
-    const int chunk = ((q >> 2) ^ sb) << 4;
-    const int within = (q & 3) << 2;
+    // column cl = 16 h + j: rows 8g .. 8g+7 as one 8-byte slot
     if (col_ok) {
+      const int slot = (g ^ h) << 3;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const uint32_t rows4[4] = {e[0][m], e[1][m], e[2][m], e[3][m]};
-        uint32_t cols4[4];
-        transpose4x4(rows4, cols4);
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo4[4] = {e[0][m], e[1][m], e[2][m], e[3][m]};
+        const uint32_t hi4[4] = {e[4][m], e[5][m], e[6][m], e[7][m]};
+        uint32_t lo[4], hi[4];
+        transpose4x4(lo4, lo);
+        transpose4x4(hi4, hi);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int cl = 32 * sb + 4 * m + jj;
-          *reinterpret_cast<uint32_t*>(lds_t + cl * kRqRows + chunk + within) = cols4[jj];
+          const int cl = 16 * h + 4 * m + jj;
+          *reinterpret_cast<uint2*>(lds_t + cl * kRqRows + slot) = make_uint2(lo[jj], hi[jj]);
         }
       }
     }
@@ -202,8 +206,10 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
       const int id = t + i * kRqThreads;
       const int cl = id >> 3, c16 = id & 7;
       if (cl < cols_in && 16 * c16 < rows_in) {
-        const uint4 v = *reinterpret_cast<const uint4*>(lds_t + cl * kRqRows + (((c16 ^ (cl >> 5)) & 7) << 4));
-        store_nt16(ot + uint32_t(cl) * Ru + 16u * c16, v);
+        // logical slots 2 c16 and 2 c16 + 1 sit in one 16-byte chunk, swapped when cl / 16 is odd
+        const int hh = (cl >> 4) & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_t + cl * kRqRows + ((((2 * c16) ^ hh) >> 1) << 4));
+        store_nt16(ot + uint32_t(cl) * Ru + 16u * c16, (hh & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v);
       }
     }
   }
@@ -217,7 +223,8 @@ hipError_t launch_rq(const RqArgs& a, uint32_t nblocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_requant(int axis, const RqArgs& a, uint32_t nblocks, hipStream_t s) {
+hipError_t launch_requant(int axis, const RqArgs& a, hipStream_t s) {
+  const uint32_t nblocks = a.total_tiles;
   switch (axis) {
     case kRow: return launch_rq<true, false>(a, nblocks, s);
     case kCol: return launch_rq<false, true>(a, nblocks, s);
