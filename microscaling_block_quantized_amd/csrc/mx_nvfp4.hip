@@ -54,9 +54,13 @@ __global__ void nv_zero_kernel(uint32_t* gs, int64_t batch) {
   if (i < batch) gs[i] = 0u;
 }
 
-constexpr int kAmaxThreads = 512;
-constexpr int kAmaxUnroll = 8;
-constexpr int kAmaxBlocks = 512;                   // workgroups over all slices: two per CU
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxUnroll = 4;
+// Workgroups over all slices: one per CU. The atomics of a persistent grid all
+// arrive at the end, about 6 ns apart on one address, so fewer and larger
+// workgroups win (measured at 16384 x 4096: 512 x 512 threads 72.2 us for the
+// whole call, 256 x 1024 69.8 us, 1024 x 256 75.1 us).
+constexpr int kAmaxBlocks = 256;
 constexpr uint32_t kNvMark = 0x80000000u;
 
 // Largest finite magnitude among a 16-byte chunk's elements, folded into m (FP32 bits).
