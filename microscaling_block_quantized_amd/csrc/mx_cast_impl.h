@@ -128,6 +128,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int CPC = BPC / 16;                // 16-byte chunks per staged column: 8 | 4
   constexpr bool CM = COLS || B2;              // column maxima needed
   constexpr bool SR = RD == kSr;
+  // stochastic rounding through the fast path, except in the FP32 row+column
+  // kernel, where the extra registers would spill
+  constexpr bool SRFAST = !(AX == kBoth && !BF16);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
   __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * kWaveRows : 4];
@@ -180,6 +183,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       out[0] = hi ? w.z : w.x;
       out[1] = hi ? w.w : w.y;
     }
+  };
+  // FP32: lanes t and t ^ 1 hold the two halves of each row's Philox block
+  // (t even: elements 0..3, words 0 and 1). Lane t computes the block of row
+  // k + (t & 1) and the pair swaps the halves the other needs (DPP), so each
+  // block is generated once for two rows.
+  auto row_draws_pair = [&](int k, uint32_t* d0, uint32_t* d1) {
+    const int p = t & 1;
+    const int64_t i0 = tile_elem + int64_t(lrow + k + p) * C + lcol;
+    const uint4 w = sr_words(uint64_t(i0) >> 3, a.seed_lo, a.seed_hi);
+    const uint32_t r0 = dpp<kDppXor1>(p ? w.x : w.z), r1 = dpp<kDppXor1>(p ? w.y : w.w);
+    d0[0] = p ? r0 : w.x;
+    d0[1] = p ? r1 : w.y;
+    d1[0] = p ? w.z : r0;
+    d1[1] = p ? w.w : r1;
   };
   constexpr bool KEEP = SR && BF16;
   uint32_t draw[KEEP ? RPT : 1][VEC / 2];
@@ -240,6 +257,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem * CB / 8;
     const uint32_t rcoff = (uint32_t(lrow) * Cu + uint32_t(lcol)) * CB / 8;
     uint32_t scale_dw = 0;                      // 4 scale bytes of one row's 128 wave columns, lane t == k
+    uint32_t dk_even[VEC / 2], dk_odd[VEC / 2];   // FP32 with SR: the draws of rows k and k + 1 (k even)
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       uint32_t m;
@@ -255,7 +273,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       const bool ok = col_ok && lrow + k < rows_in;
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu * CB / 8;
       if constexpr (BF16) {
-        const uint2 w = SR ? encode8_sr<true, F, M>(v[k], draw[KEEP ? k : 0], code)
+        const uint2 w = SR ? encode8_sr<true, F, M, SRFAST>(v[k], draw[KEEP ? k : 0], code)
                            : encode8_bf16<F, M>(v[k].x, v[k].y, v[k].z, v[k].w, code);
         if constexpr (CB == 6) {
           // 48 bits per lane: even lanes store theirs and the odd neighbour's as 12 bytes
@@ -270,9 +288,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       } else {
         uint32_t w;
         if constexpr (SR) {
-          uint32_t dk[VEC / 2];
-          row_draws(k, dk);
-          w = encode8_sr<false, F, M>(v[k], dk, code).x;
+          if ((k & 1) == 0) row_draws_pair(k, dk_even, dk_odd);
+          w = encode8_sr<false, F, M, SRFAST>(v[k], (k & 1) ? dk_odd : dk_even, code).x;
         } else {
           w = encode4_f32<F, M>(__uint_as_float(v[k].x), __uint_as_float(v[k].y), __uint_as_float(v[k].z),
                                 __uint_as_float(v[k].w), code);
@@ -349,15 +366,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int g = 0; g < RPT / 4; ++g) {
         uint32_t dr[4][VEC / 2];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) row_draws(4 * g + r, dr[r]);
+        row_draws_pair(4 * g, dr[0], dr[1]);
+        row_draws_pair(4 * g + 2, dr[2], dr[3]);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const int e = int(code_j[j]) - 127;
           float f[4];
+          uint32_t xb[4], uu[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            f[r] = sr_scaled<F>((&v[4 * g + r].x)[j], e, (j & 1) ? (dr[r][j >> 1] >> 16) : (dr[r][j >> 1] & 0xFFFFu));
+          for (int r = 0; r < 4; ++r) {
+            xb[r] = (&v[4 * g + r].x)[j];
+            uu[r] = (j & 1) ? (dr[r][j >> 1] >> 16) : (dr[r][j >> 1] & 0xFFFFu);
+          }
+          sr_scaled_n<F, 4, SRFAST>(xb, e, uu, f);
           w[j][g] = encode4_f32<F, M>(f[0], f[1], f[2], f[3], sr_enc_code(code_j[j]));
         }
       }
@@ -386,7 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           uint32_t dj[RPT];
 #pragma unroll
           for (int k = 0; k < RPT; ++k) dj[k] = (j & 1) ? (draw[KEEP ? k : 0][j >> 1] >> 16) : (draw[KEEP ? k : 0][j >> 1] & 0xFFFFu);
-          w = encode_col_sr<F, M>(pr, dj, code_j[j]);
+          w = encode_col_sr<F, M, SRFAST>(pr, dj, code_j[j]);
         } else {
           w = encode8_bf16<F, M>(pr[0], pr[1], pr[2], pr[3], code_j[j]);
         }
@@ -517,7 +538,7 @@ __global__ __launch_bounds__(kRowThreads) void mx_cast_rows_kernel(CastArgs a, i
       for (int j = 0; j < VEC / 2; ++j) draw[j] = (h + j) == 0 ? w.x : (h + j) == 1 ? w.y : (h + j) == 2 ? w.z : w.w;
     }
     if constexpr (BF16) {
-      const uint2 w = RD == kSr ? encode8_sr<true, F, M>(v[u], draw, code) : encode8_bf16<F, M>(v[u].x, v[u].y, v[u].z, v[u].w, code);
+      const uint2 w = RD == kSr ? encode8_sr<true, F, M, true>(v[u], draw, code) : encode8_bf16<F, M>(v[u].x, v[u].y, v[u].z, v[u].w, code);
       if constexpr (CB == 6) {
         // even lanes store their 48 bits and the odd neighbour's as 12 bytes
         const uint32_t hi = pack6(w.y);
@@ -529,7 +550,7 @@ __global__ __launch_bounds__(kRowThreads) void mx_cast_rows_kernel(CastArgs a, i
         else store_nt4(dst, w.x);
       }
     } else {
-      const uint32_t w = RD == kSr ? encode8_sr<false, F, M>(v[u], draw, code).x
+      const uint32_t w = RD == kSr ? encode8_sr<false, F, M, true>(v[u], draw, code).x
                                    : encode4_f32<F, M>(__uint_as_float(v[u].x), __uint_as_float(v[u].y),
                                                        __uint_as_float(v[u].z), __uint_as_float(v[u].w), code);
       if constexpr (CB == 6) {

@@ -93,6 +93,88 @@ __device__ __forceinline__ float sr_scaled(uint32_t xb, int e, uint32_t u) {
   return __uint_as_float(sign | __float_as_uint(v));
 }
 
+// sr_scaled without branches: |x| = M * 2^lsb and the grid spacing at |x| is
+// 2^eq, so with d = eq - lsb the grid index below |x| is n = M >> d and the
+// fraction is the d low bits of M. That fraction scaled by 2^32 is compared
+// with u * 2^16: for d <= 32 it is M << (32 - d) exactly; for d > 32 it is
+// M >> (d - 32) plus a sticky bit for the bits shifted out, which decides the
+// tie. All 32-bit.
+template <int F>
+__device__ __forceinline__ float sr_scaled_flat(uint32_t xb, int e, uint32_t u) {
+  const uint32_t ab = xb & 0x7FFFFFFFu;
+  const uint32_t sign = xb & 0x80000000u;
+  const float lim = __builtin_ldexpf(SrC<F>::vmax, e);          // exact, or +Inf
+  const uint32_t field = ab >> 23;
+  const uint32_t mant = field ? ((ab & 0x7FFFFFu) | 0x800000u) : ab;
+  const int lsb = (field ? int(field) : 1) - 150;
+  int eq;
+  if constexpr (F == kInt8) {
+    eq = e - 6;
+  } else {
+    const int top = field ? int(field) - 127 : (31 - __builtin_clz(mant | 1u)) - 149;   // floor(log2 |x|)
+    eq = max(top, e + SrC<F>::emin) - SrC<F>::mbits;
+  }
+  const int d = eq - lsb;
+  const uint32_t n = d <= 0 ? mant << uint32_t(min(-d, 31)) : (d >= 32 ? 0u : mant >> uint32_t(d));
+  const uint32_t sh = uint32_t(min(max(d - 32, 0), 24));
+  const uint32_t rem = d <= 32 ? mant << uint32_t(min(max(32 - d, 0), 31)) : mant >> sh;
+  const bool lost = d > 32 && (mant & ((1u << sh) - 1u)) != 0u;
+  const uint32_t thr = u << 16;
+  const bool up = d >= 1 && (rem > thr || (rem == thr && lost));
+  const float v = float(n + (up ? 1u : 0u)) * __uint_as_float(uint32_t(eq - e + 127) << 23);
+  uint32_t r = ab == 0u ? xb : (sign | __float_as_uint(v));
+  r = __uint_as_float(ab) < lim ? r : (sign | __float_as_uint(SrC<F>::vmax));
+  return __uint_as_float(r);
+}
+
+// The same for every input but FP32 subnormals, with fewer operations: x
+// zero, saturating, or normal. A normal x below saturation has d >= 17 (the
+// spacing is at least 2^(23 - mbits) of its ulps; INT8: 2^17), so the
+// d <= 0 case and the leading-zero count of sr_scaled_flat drop out. Sets
+// `slow` for a subnormal x, and the caller then recomputes with
+// sr_scaled_flat.
+template <int F>
+__device__ __forceinline__ float sr_scaled_fast(uint32_t xb, int e, float lim, uint32_t u, bool& slow) {
+  const uint32_t ab = xb & 0x7FFFFFFFu;
+  const int field = int(ab >> 23);
+  int eq;
+  if constexpr (F == kInt8) eq = e - 6;
+  else eq = max(field - 127, e + SrC<F>::emin) - SrC<F>::mbits;
+  const int d = eq - field + 150;
+  const uint32_t mant = (ab & 0x7FFFFFu) | 0x800000u;
+  const uint32_t n = mant >> uint32_t(min(max(d, 0), 31));
+  const uint32_t sh = uint32_t(min(max(d - 32, 0), 24));
+  const uint32_t rem = d <= 32 ? mant << uint32_t((32 - d) & 31) : mant >> sh;
+  const bool lost = d > 32 && (mant & ((1u << sh) - 1u)) != 0u;
+  const uint32_t thr = u << 16;
+  const bool up = rem > thr || (rem == thr && lost);
+  const float v = float(n + (up ? 1u : 0u)) * __uint_as_float(uint32_t(eq - e + 127) << 23);
+  const bool sat = !(__uint_as_float(ab) < lim);
+  slow |= field == 0 && ab != 0u;
+  const uint32_t mag = sat ? __float_as_uint(SrC<F>::vmax) : __float_as_uint(v);
+  return __uint_as_float(ab == 0u ? xb : ((xb & 0x80000000u) | mag));
+}
+
+// N elements. FAST: through the fast path, redone with sr_scaled_flat when any
+// lane of the wave needs it (one branch per group). Otherwise sr_scaled per
+// element, which needs the fewest registers (the FP32 row+column kernel).
+template <int F, int N, bool FAST>
+__device__ __forceinline__ void sr_scaled_n(const uint32_t* xb, int e, const uint32_t* u, float* f) {
+  if constexpr (FAST) {
+    const float lim = __builtin_ldexpf(SrC<F>::vmax, e);
+    bool slow = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = sr_scaled_fast<F>(xb[i], e, lim, u[i], slow);
+    if (slow) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) f[i] = sr_scaled_flat<F>(xb[i], e, u[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = sr_scaled<F>(xb[i], e, u[i]);
+  }
+}
+
 // Scale code for encoding values that sr_scaled already divided by 2^e: 2^0,
 // or the NaN code that makes the encoders write a NaN block.
 __device__ __forceinline__ uint32_t sr_enc_code(uint32_t code) { return code == 0xFFu ? 0xFFu : 127u; }
@@ -101,42 +183,50 @@ __device__ __forceinline__ uint32_t sr_enc_code(uint32_t code) { return code == 
 // is first moved onto the grid (sr_scaled), which the nearest-even encoder then
 // maps to its own code. Output layout as encode8_bf16 (BF16: 8 elements) or
 // encode4_f32 (FP32: 4 elements, in .x).
-template <bool BF16, int F, int M>
+template <bool BF16, int F, int M, bool FAST>
 __device__ __forceinline__ uint2 encode8_sr(const uint4& v, const uint32_t* draw, uint32_t code) {
   const int e = int(code) - 127;
   const uint32_t ec = sr_enc_code(code);
   if constexpr (BF16) {
     float f[8];
+    uint32_t xb[8], uu[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t p = (&v.x)[i];
-      f[2 * i] = sr_scaled<F>(p << 16, e, draw[i] & 0xFFFFu);
-      f[2 * i + 1] = sr_scaled<F>(p & 0xFFFF0000u, e, draw[i] >> 16);
+      xb[2 * i] = p << 16;
+      xb[2 * i + 1] = p & 0xFFFF0000u;
+      uu[2 * i] = draw[i] & 0xFFFFu;
+      uu[2 * i + 1] = draw[i] >> 16;
     }
+    sr_scaled_n<F, 8, FAST>(xb, e, uu, f);
     const uint32_t lo = encode4_f32<F, M>(f[0], f[1], f[2], f[3], ec);
     const uint32_t hi = encode4_f32<F, M>(f[4], f[5], f[6], f[7], ec);
     if constexpr (F == kE2M1) return make_uint2((lo & 0xFFFFu) | (hi << 16), 0u);
     else return make_uint2(lo, hi);
   } else {
     float f[4];
+    uint32_t uu[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = sr_scaled<F>((&v.x)[i], e, (i & 1) ? (draw[i >> 1] >> 16) : (draw[i >> 1] & 0xFFFFu));
+    for (int i = 0; i < 4; ++i) uu[i] = (i & 1) ? (draw[i >> 1] >> 16) : (draw[i >> 1] & 0xFFFFu);
+    sr_scaled_n<F, 4, FAST>(&v.x, e, uu, f);
     return make_uint2(encode4_f32<F, M>(f[0], f[1], f[2], f[3], ec), 0u);
   }
 }
 
 // One column of 8 BF16 rows (pairs pr[i] = rows 2i (low half) and 2i+1) with
 // the rows' draws dj[0..7].
-template <int F, int M>
+template <int F, int M, bool FAST>
 __device__ __forceinline__ uint2 encode_col_sr(const uint32_t* pr, const uint32_t* dj, uint32_t code) {
   const int e = int(code) - 127;
   const uint32_t ec = sr_enc_code(code);
   float f[8];
+  uint32_t xb[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = sr_scaled<F>(pr[i] << 16, e, dj[2 * i]);
-    f[2 * i + 1] = sr_scaled<F>(pr[i] & 0xFFFF0000u, e, dj[2 * i + 1]);
+    xb[2 * i] = pr[i] << 16;
+    xb[2 * i + 1] = pr[i] & 0xFFFF0000u;
   }
+  sr_scaled_n<F, 8, FAST>(xb, e, dj, f);
   const uint32_t lo = encode4_f32<F, M>(f[0], f[1], f[2], f[3], ec);
   const uint32_t hi = encode4_f32<F, M>(f[4], f[5], f[6], f[7], ec);
   if constexpr (F == kE2M1) return make_uint2((lo & 0xFFFFu) | (hi << 16), 0u);
