@@ -122,19 +122,59 @@ def summarize_trace(stats_csv: str, command: str, workload: str = "activations")
     return "\n".join(out) + "\n"
 
 
+# per workload, for the counter summaries: (kernel-name substring, short name,
+# algorithmic bytes read, algorithmic bytes written) per launch
+COUNTER_KERNELS = {
+    "act_nvfp4": [("nv_amax_kernel<true>", "nv_amax_kernel<bf16>", _NV_N * 2, 0),
+                  ("nv_cast_kernel<true, 3>", "nv_cast_kernel<bf16,row+col>", _NV_N * 2, 2 * (_NV_N // 2 + _NV_N // 16))],
+    "weights_fp4_in_fp8": [("requant_kernel<true, true>", "requant_kernel<row+col>", _RQ_N // 2 + _RQ_N // 32,
+                            2 * (_RQ_N + 4 * (_RQ_N // 16384)) + _RQ_N // 16384)],
+}
+
+
+def _counter_means(path, counter, keys):
+    acc = {}
+    for r in _csv_rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        for sub_, key in keys:
+            if sub_ in r["Kernel_Name"]:
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+                break
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_counters_of(fetch_csv: str, write_csv: str, command: str, workload: str) -> str:
+    """Per-kernel calibrated HBM bytes for one of the other workloads (see summarize_counters)."""
+    kernels = COUNTER_KERNELS[workload]
+    keys = [(k[0], k[1]) for k in kernels] + [(COPY_KERNEL, "copy")]
+    copy_each_way = copy_bytes(WORKLOADS[workload]["bytes"])
+    f = _counter_means(fetch_csv, "FETCH_SIZE", keys)
+    w = _counter_means(write_csv, "WRITE_SIZE", keys)
+    f_cal = copy_each_way / (f["copy"] * 1024.0)
+    w_cal = copy_each_way / (w["copy"] * 1024.0)
+    lines = [f"# rocprofv3 HBM counters: {TRACE_KERNELS[workload][0]}", "",
+             f"command (FETCH_SIZE): {command.format(counter='FETCH_SIZE')}",
+             f"command (WRITE_SIZE): {command.format(counter='WRITE_SIZE')}", "",
+             f"calibration: torch copy kernel {COPY_KERNEL} moving {copy_each_way} B each way reads "
+             f"FETCH_SIZE {f['copy']:.1f} KiB (factor {f_cal:.4f}) and WRITE_SIZE {w['copy']:.1f} KiB "
+             f"(factor {w_cal:.4f})", "",
+             "| kernel | fetched B (calibrated) | algorithmic read | ratio | written B (calibrated) | "
+             "algorithmic write | ratio |", "|---|---|---|---|---|---|---|"]
+    for _, short, rd, wr in kernels:
+        fb = f[short] * 1024.0 * f_cal
+        wb = w[short] * 1024.0 * w_cal
+        lines.append(f"| {short} | {fb:.0f} | {rd} | {fb / rd:.4f} | {wb:.0f} | {wr} | "
+                     f"{(wb / wr) if wr else float('nan'):.4f} |")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     """HBM bytes per launch of the cast from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for torch's copy kernel
     moving a known number of bytes in the same run."""
     def per_kernel(path, counter):
-        acc = {}
-        for r in _csv_rows(path):
-            if r["Counter_Name"] != counter:
-                continue
-            key = "cast" if CAST_KERNEL in r["Kernel_Name"] else ("copy" if COPY_KERNEL in r["Kernel_Name"] else None)
-            if key:
-                acc.setdefault(key, []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in acc.items()}
+        return _counter_means(path, counter, [(CAST_KERNEL, "cast"), (COPY_KERNEL, "copy")])
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
     f_cal = COPY_BYTES / (f["copy"] * 1024.0)
@@ -386,13 +426,16 @@ def main() -> int:
                     help="print the calibrated HBM-traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--trace-workload", default="activations", choices=sorted(TRACE_KERNELS),
-                    help="which workload's kernels --summarize-trace reports")
+                    help="which workload's kernels --summarize-trace / --summarize-counters report")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.command, args.trace_workload), end="")
         return 0
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters, args.command), end="")
+        if args.trace_workload == "activations":
+            print(summarize_counters(*args.summarize_counters, args.command), end="")
+        else:
+            print(summarize_counters_of(*args.summarize_counters, args.command, args.trace_workload), end="")
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MX cast needs no "
