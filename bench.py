@@ -311,6 +311,34 @@ def _requant_workload():
             "config": {"workload": desc, "rows": r, "cols": c, "fmt": "e2m1->e4m3", "axis": "both"}}
 
 
+def _qat_workload():
+    """14336x4096 FP32 master weights -> MXFP4 (E2M1 1x32, floor) -> FP8 E4M3 with
+    128x128 block scales, one pass: the MXFP4 plane, both FP8 copies and the
+    spreads are written."""
+    r, c = 14336, 4096
+    n = r * c
+    nblk = (r // 128) * (c // 128)
+    nbytes = 4 * n + (n // 2 + n // 32) + 2 * (n + 4 * nblk) + nblk
+
+    def make(dev, i):
+        import torch
+        import microscaling_block_quantized_amd as mx
+        import mx_inputs as I
+        x = I.weights(r, c, seed=2 + 100 * i, device=dev).float()
+        out = {"fp4_codes": torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
+               "fp4_scales": torch.empty((r, c // 32), dtype=torch.uint8, device=dev),
+               "e4m3": torch.empty((r, c), dtype=torch.uint8, device=dev),
+               "block_scale": torch.empty((r // 128, c // 128), dtype=torch.float32, device=dev),
+               "e4m3_t": torch.empty((c, r), dtype=torch.uint8, device=dev),
+               "block_scale_t": torch.empty((c // 128, r // 128), dtype=torch.float32, device=dev),
+               "spread": torch.empty((r // 128, c // 128), dtype=torch.uint8, device=dev)}
+        return mx.BoundQuantizeFp4Fp8(x, "floor", "both", out)
+    desc = ("FP32 master weights 14336x4096 -> MXFP4 (E2M1 1x32, floor) -> FP8 E4M3 with 128x128 power-of-two "
+            "block scales in one pass: MXFP4 plane + row copy + transposed copy + spreads")
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+            "config": {"workload": desc, "rows": r, "cols": c, "fmt": "f32->e2m1->e4m3", "axis": "both"}}
+
+
 def _wide_range_pipeline():
     """64 x 4096x14336 BF16: fused E4M3 quantize, then both planes dequantized to BF16."""
     b, r, c = 64, 4096, 14336
@@ -403,6 +431,7 @@ WORKLOADS = {
                                       "floor scale rule", block="32x32"),
     "act_nvfp4": _nvfp4_workload(),
     "weights_fp4_in_fp8": _requant_workload(),
+    "qat_fp4_fp8": _qat_workload(),
     "wide_range": _wide_range_pipeline(),
     "fp32_normal": _fp32_normal_round_trip(),
 }

@@ -222,6 +222,19 @@ int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* g
 int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_axis axis, uint8_t* fp8,
                        float* block_scale, uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream);
 
+/* The quantization-aware step of the same section in one pass: master weights
+ * x (BF16 or FP32, [batch][rows][cols]) are cast to MXFP4 exactly as
+ * mx_quantize does with fmt = MX_FMT_E2M1, scale rule scale_mode and
+ * MX_AXIS_ROW, and that MXFP4 plane is re-expressed as FP8 exactly as
+ * mx_requant_fp4_fp8 does; the result equals the two calls in sequence.
+ *   fp4_codes / fp4_scales  the MXFP4 plane ([batch][rows][cols/2], 8-byte
+ *                aligned; [batch][rows][cols/32]), both or neither (NULL: not stored)
+ *   fp8, block_scale, fp8_t, block_scale_t, spread  as for mx_requant_fp4_fp8
+ * x 16-byte aligned; cols % 32 == 0; rows % 16 == 0 with MX_AXIS_COL. */
+int mx_quantize_fp4_fp8(const void* x, mx_dtype x_dtype, mx_shape s, mx_scale_mode scale_mode, mx_axis axis,
+                        void* fp4_codes, uint8_t* fp4_scales, uint8_t* fp8, float* block_scale, uint8_t* fp8_t,
+                        float* block_scale_t, uint8_t* spread, void* stream);
+
 /* Static text for an MX_* code; never NULL. */
 const char* mx_strerror(int err);
 

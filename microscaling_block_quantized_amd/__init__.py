@@ -24,7 +24,8 @@ import os
 __all__ = [
     "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "ROUNDING", "BLOCK", "MxQuantOpts", "lib_path", "load", "mx_version", "mx_strerror",
     "mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_quantize_nvfp4", "mx_dequantize_nvfp4",
-    "mx_requant_fp4_fp8", "EXPORTS", "BoundQuantize", "BoundDequantize", "BoundQuantizeNvfp4", "BoundRequant",
+    "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "EXPORTS", "BoundQuantize", "BoundDequantize",
+    "BoundQuantizeNvfp4", "BoundRequant", "BoundQuantizeFp4Fp8",
 ]
 
 FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e2m3": 3, "e3m2": 4, "int8": 5}
@@ -35,7 +36,8 @@ ROUNDING = {"rne": 0, "sr": 1}
 BLOCK = {"1x32": 0, "32x32": 1}
 DTYPE = {"f32": 0, "bf16": 1}
 EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_quantize_ex", "mx_dequantize", "mx_dequantize_ex",
-           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_requant_fp4_fp8", "mx_strerror", "mx_version")
+           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "mx_strerror",
+           "mx_version")
 
 _LIB = None
 
@@ -91,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.mx_dequantize_nvfp4.argtypes = [vp, u8p, vp, MxShape, i32, vp, vp]
     lib.mx_requant_fp4_fp8.restype = i32
     lib.mx_requant_fp4_fp8.argtypes = [vp, u8p, MxShape, i32, u8p, vp, u8p, vp, u8p, vp]
+    lib.mx_quantize_fp4_fp8.restype = i32
+    lib.mx_quantize_fp4_fp8.argtypes = [vp, i32, MxShape, i32, i32, vp, u8p, u8p, vp, u8p, vp, u8p, vp]
     _LIB = lib
     return lib
 
@@ -406,3 +410,50 @@ class BoundRequant:
         err = self._fn(*self._args)
         if err:
             raise MXError(err, "mx_requant_fp4_fp8")
+
+
+def mx_quantize_fp4_fp8(x, mode: str = "floor", axis: str = "both", fp4: bool = True, spread: bool = True,
+                        out: dict | None = None):
+    """Master weights x (GPU, bfloat16 or float32, [R][C] or [B][R][C]) ->
+    MXFP4 (E2M1, 1x32, scale rule ``mode``) -> FP8 with 128x128 block scales, in
+    one pass. Returns the planes of mx_requant_fp4_fp8 plus, with ``fp4``,
+    "fp4_codes" [..][R][C/2] and "fp4_scales" [..][R][C/32]."""
+    import torch
+    if not x.is_cuda:
+        raise ValueError("mx_quantize_fp4_fp8 needs a GPU tensor (libmx has no CPU path)")
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_contiguous():
+        raise TypeError("input must be a contiguous bfloat16 or float32 tensor")
+    b, r, c = _shape3(x.shape)
+    planes = _rq_planes(x, tuple(x.shape), axis, spread, out)
+    if fp4:
+        lead = (b,) if x.dim() == 3 else ()
+        planes.setdefault("fp4_codes", torch.empty(lead + (r, c // 2), dtype=torch.uint8, device=x.device))
+        planes.setdefault("fp4_scales", torch.empty(lead + (r, c // 32), dtype=torch.uint8, device=x.device))
+    with torch.cuda.device(x.device):
+        err = load().mx_quantize_fp4_fp8(
+            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), MODE[mode], AXIS[axis],
+            _ptr(planes.get("fp4_codes")), _ptr(planes.get("fp4_scales")), _ptr(planes.get("e4m3")),
+            _ptr(planes.get("block_scale")), _ptr(planes.get("e4m3_t")), _ptr(planes.get("block_scale_t")),
+            _ptr(planes.get("spread")), _stream_of(x))
+    if err:
+        raise MXError(err, "mx_quantize_fp4_fp8")
+    return planes
+
+
+class BoundQuantizeFp4Fp8:
+    """An mx_quantize_fp4_fp8 call marshalled once (see BoundQuantize)."""
+
+    def __init__(self, x, mode: str, axis: str, out: dict):
+        import torch
+        b, r, c = _shape3(x.shape)
+        self._fn = load().mx_quantize_fp4_fp8
+        self._args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), MODE[mode],
+                      AXIS[axis], _ptr(out.get("fp4_codes")), _ptr(out.get("fp4_scales")), _ptr(out.get("e4m3")),
+                      _ptr(out.get("block_scale")), _ptr(out.get("e4m3_t")), _ptr(out.get("block_scale_t")),
+                      _ptr(out.get("spread")), _stream_of(x))
+        self._keep = (x, out)
+
+    def __call__(self) -> None:
+        err = self._fn(*self._args)
+        if err:
+            raise MXError(err, "mx_quantize_fp4_fp8")

@@ -55,7 +55,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10400; }
+int mx_version(void) { return 10500; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -250,25 +250,38 @@ int mx_dequantize_nvfp4(const void* codes, const uint8_t* scales, const float* g
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
-int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_axis axis, uint8_t* fp8,
-                       float* block_scale, uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream) {
-  if (!valid_axis(axis)) return MX_ERR_ENUM;
+// Shared by the two FP8-block entry points: the source is an MXFP4 plane
+// (codes, scales) or master weights x (cast to MXFP4 on the way, optionally
+// written to fp4_codes / fp4_scales).
+static int rq_launch(int src, int mode, const void* x, const void* codes, const uint8_t* scales, uint8_t* fp4_codes,
+                     uint8_t* fp4_scales, mx_shape s, mx_axis axis, uint8_t* fp8, float* block_scale,
+                     uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream) {
   const bool want_row = (axis & MX_AXIS_ROW) != 0;
   const bool want_col = (axis & MX_AXIS_COL) != 0;
-  if (codes == nullptr || scales == nullptr) return MX_ERR_NULL;
+  const bool from_mx = src == mx::kFromMx;
+  const int64_t xes = src == mx::kFromF32 ? 4 : 2;
+  if (from_mx ? (codes == nullptr || scales == nullptr) : x == nullptr) return MX_ERR_NULL;
+  if ((fp4_codes != nullptr) != (fp4_scales != nullptr)) return MX_ERR_NULL;
   if (want_row != (fp8 != nullptr) || want_row != (block_scale != nullptr)) return MX_ERR_NULL;
   if (want_col != (fp8_t != nullptr) || want_col != (block_scale_t != nullptr)) return MX_ERR_NULL;
   const int64_t n = elements(s);
   if (n < 0 || s.cols % kBlock != 0 || (want_col && s.rows % 16 != 0)) return MX_ERR_SHAPE;
-  if (!aligned(codes, 16) || (want_row && (!aligned(fp8, 16) || !aligned(block_scale, 4))) ||
+  if ((from_mx && !aligned(codes, 16)) || (!from_mx && !aligned(x, 16)) ||
+      (fp4_codes != nullptr && !aligned(fp4_codes, 8)) ||
+      (want_row && (!aligned(fp8, 16) || !aligned(block_scale, 4))) ||
       (want_col && (!aligned(fp8_t, 16) || !aligned(block_scale_t, 4))))
     return MX_ERR_ALIGN;
   const int64_t nbr = (s.rows + 127) / 128, nbc = (s.cols + 127) / 128;
   const int64_t nblk = s.batch * nbr * nbc;
-  Range rs[7];
+  Range rs[8];
   int nr = 0;
-  rs[nr++] = range_of(codes, n / 2);
-  rs[nr++] = range_of(scales, n / kBlock);
+  if (from_mx) {
+    rs[nr++] = range_of(codes, n / 2);
+    rs[nr++] = range_of(scales, n / kBlock);
+  } else {
+    rs[nr++] = range_of(x, n * xes);
+    if (fp4_codes != nullptr) { rs[nr++] = range_of(fp4_codes, n / 2); rs[nr++] = range_of(fp4_scales, n / kBlock); }
+  }
   if (want_row) { rs[nr++] = range_of(fp8, n); rs[nr++] = range_of(block_scale, nblk * 4); }
   if (want_col) { rs[nr++] = range_of(fp8_t, n); rs[nr++] = range_of(block_scale_t, nblk * 4); }
   if (spread != nullptr) rs[nr++] = range_of(spread, nblk);
@@ -283,6 +296,9 @@ int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_
   mx::RqArgs a;
   a.codes = static_cast<const uint8_t*>(codes);
   a.scales = scales;
+  a.x = x;
+  a.out_codes = fp4_codes;
+  a.out_scales = fp4_scales;
   a.fp8 = fp8;
   a.block_scale = block_scale;
   a.fp8_t = fp8_t;
@@ -293,8 +309,25 @@ int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_
   a.tiles_r = uint32_t(tiles_r);
   a.tiles_c = uint32_t(tiles_c);
   a.total_tiles = uint32_t(blocks);
-  const hipError_t e = mx::launch_requant(int(axis), a, static_cast<hipStream_t>(stream));
+  const hipError_t e = mx::launch_requant(src, mode, int(axis), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_axis axis, uint8_t* fp8,
+                       float* block_scale, uint8_t* fp8_t, float* block_scale_t, uint8_t* spread, void* stream) {
+  if (!valid_axis(axis)) return MX_ERR_ENUM;
+  return rq_launch(mx::kFromMx, mx::kFloor, nullptr, codes, scales, nullptr, nullptr, s, axis, fp8, block_scale,
+                   fp8_t, block_scale_t, spread, stream);
+}
+
+int mx_quantize_fp4_fp8(const void* x, mx_dtype x_dtype, mx_shape s, mx_scale_mode scale_mode, mx_axis axis,
+                        void* fp4_codes, uint8_t* fp4_scales, uint8_t* fp8, float* block_scale, uint8_t* fp8_t,
+                        float* block_scale_t, uint8_t* spread, void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_mode(scale_mode) || !valid_axis(axis)) return MX_ERR_ENUM;
+  return rq_launch(x_dtype == MX_BF16 ? mx::kFromBf16 : mx::kFromF32,
+                   scale_mode == MX_SCALE_ROUNDUP ? mx::kRoundUp : mx::kFloor, x, nullptr, nullptr,
+                   static_cast<uint8_t*>(fp4_codes), fp4_scales, s, axis, fp8, block_scale, fp8_t, block_scale_t,
+                   spread, stream);
 }
 
 }  // extern "C"

@@ -71,8 +71,11 @@ hipError_t launch_nvfp4_dequant(bool out_bf16, const uint8_t* codes, const uint8
 // byte, E8M0 scales per 32 elements along cols) into E4M3 with one FP32 scale
 // per 128x128 block (mx_requant.hip).
 struct RqArgs {
-  const uint8_t* codes;        // [batch][rows][cols/2]
-  const uint8_t* scales;       // [batch][rows][cols/32]
+  const uint8_t* codes;        // [batch][rows][cols/2]   (source kFromMx)
+  const uint8_t* scales;       // [batch][rows][cols/32]  (source kFromMx)
+  const void* x;               // [batch][rows][cols] BF16 / FP32 master weights (kFromBf16 / kFromF32)
+  uint8_t* out_codes;          // the MXFP4 plane cast from x, or null
+  uint8_t* out_scales;
   uint8_t* fp8;                // [batch][rows][cols] or null
   float* block_scale;          // [batch][R'][C'] or null (R' = ceil(rows/128), C' = ceil(cols/128))
   uint8_t* fp8_t;              // [batch][cols][rows] or null
@@ -82,7 +85,9 @@ struct RqArgs {
   uint32_t tiles_r, tiles_c;   // 128-row x 256-column tiles per slice
   uint32_t total_tiles;        // batch * tiles_r * tiles_c: one workgroup each
 };
-hipError_t launch_requant(int axis, const RqArgs& a, hipStream_t s);
+enum RqSource : int { kFromMx = 0, kFromBf16 = 1, kFromF32 = 2 };
+// mode: the MXFP4 scale rule (kFloor / kRoundUp) when casting from x.
+hipError_t launch_requant(int src, int mode, int axis, const RqArgs& a, hipStream_t s);
 
 // Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
 // or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10400
+    assert mxb.mx_version() == 10500
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -223,3 +223,28 @@ def test_requant_argument_errors(lib):
     assert rq(bt=F_ + 16) == E_ALIAS
     assert rq(shape=(1, 1, 1 << 22), axis=1, ft=0, bt=0) == E_BIG
     assert rq(shape=(1, 1 << 23, 32)) == E_BIG                   # transposed rows too long
+
+
+def test_quantize_fp4_fp8_argument_errors(lib):
+    """mx_quantize_fp4_fp8: every case fails validation (addresses 4 GiB apart)."""
+    v = lambda p: ctypes.c_void_p(p)
+    G = 1 << 32
+    X_, C_, S_, F_, B_, FT, BT, SP = (G * k for k in range(1, 9))
+
+    def qq(x=X_, dt=0, shape=(1, 64, 64), mode=0, axis=3, c=C_, s=S_, f=F_, b=B_, ft=FT, bt=BT, sp=SP):
+        return lib.mx_quantize_fp4_fp8(v(x), dt, MxShape(*shape), mode, axis, v(c), v(s), v(f), v(b), v(ft), v(bt),
+                                       v(sp), None)
+    assert qq(dt=2) == E_ENUM
+    assert qq(mode=2) == E_ENUM
+    assert qq(axis=0) == E_ENUM
+    assert qq(x=0) == E_NULL
+    assert qq(s=0) == E_NULL                                     # MXFP4 codes without their scales
+    assert qq(axis=1) == E_NULL                                  # column planes without the column axis
+    assert qq(shape=(1, 64, 48)) == E_SHAPE
+    assert qq(shape=(1, 40, 64)) == E_SHAPE
+    # no MXFP4 plane and the row copy alone accept 40 rows: the alias check after it fails
+    assert qq(shape=(1, 40, 64), axis=1, c=0, s=0, ft=0, bt=0, f=X_ + 16) == E_ALIAS
+    assert qq(x=X_ + 8) == E_ALIGN
+    assert qq(c=C_ + 4) == E_ALIGN
+    assert qq(c=X_ + 64) == E_ALIAS                              # MXFP4 codes over the weights
+    assert qq(shape=(1, 1, 1 << 22), axis=1, ft=0, bt=0) == E_BIG

@@ -150,3 +150,77 @@ def test_full_size_weights(mx):
         assert np.array_equal(out["e4m3_t"][:, r0:r0 + 256].cpu().numpy(), exp["e4m3_t"])
         assert np.array_equal(out["block_scale_t"][:, b0:b0 + 2].cpu().numpy().view(np.uint32),
                               exp["block_scale_t"].view(np.uint32))
+
+
+# ---------------- one pass from the master weights ----------------
+
+OMODE = {"floor": O.FLOOR, "roundup": O.ROUNDUP}
+
+
+def qat_oracle(x, mode):
+    dt = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    q = O.quantize(I.to_bits(x), dt, O.E2M1, OMODE[mode], O.ROW)
+    exp = O.requant_fp4_to_fp8(q["row_codes"], q["row_scales"])
+    exp["fp4_codes"], exp["fp4_scales"] = q["row_codes"], q["row_scales"]
+    if x.dim() == 2:
+        exp = {k: v[0] for k, v in exp.items()}
+    return exp
+
+
+def check_qat(mx, x, mode, axis, what):
+    out = mx.mx_quantize_fp4_fp8(x.cuda().contiguous(), mode, axis)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    exp = qat_oracle(x, mode)
+    compare(got, exp, axis, what)
+    for key in ("fp4_codes", "fp4_scales"):
+        assert np.array_equal(got[key], exp[key]), (what, key)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["floor", "roundup"])
+@pytest.mark.parametrize("axis", ["row", "col", "both"])
+def test_qat_shapes(mx, axis, mode, dt):
+    for b, r, c in [(1, 128, 256), (1, 208, 160), (2, 272, 544), (1, 16, 32), (1, 400, 4128)]:
+        x = torch.stack([I.weights(r, c, seed=80 + i) for i in range(b)])
+        x = x.float() if dt == "f32" else x
+        check_qat(mx, x if b > 1 else x[0], mode, axis, f"{(b, r, c)}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_qat_specials_and_wide_range(mx, dt):
+    g = I.gradients(288, 320, seed=81)                           # zeros, NaN, Inf, zero blocks
+    check_qat(mx, g if dt == "f32" else g.to(torch.bfloat16), "floor", "both", "gradients")
+    w = torch.stack([I.wide_range(i, 256, 384, seed=82) for i in range(2)])
+    check_qat(mx, w.float() if dt == "f32" else w, "roundup", "both", "wide range")
+    e = I.fp32_edges("e2m1")
+    e = e[: (e.shape[0] // 16) * 16]
+    check_qat(mx, e if dt == "f32" else e.to(torch.bfloat16), "floor", "both", "edges")
+
+
+def test_qat_equals_the_two_calls(mx):
+    x = I.weights(512, 768, seed=83).float().cuda()
+    one = mx.mx_quantize_fp4_fp8(x, "floor", "both")
+    q = mx.mx_quantize(x, "e2m1", "floor", "row")
+    two = mx.mx_requant_fp4_fp8(q["row_codes"], q["row_scales"], (512, 768), "both")
+    torch.cuda.synchronize()
+    assert torch.equal(one["fp4_codes"], q["row_codes"]) and torch.equal(one["fp4_scales"], q["row_scales"])
+    for k in ("e4m3", "block_scale", "e4m3_t", "block_scale_t", "spread"):
+        assert torch.equal(one[k], two[k]), k
+
+
+def test_qat_full_size_fp32_master(mx):
+    """14336x4096 FP32 master weights, both copies, sampled 256-row slabs."""
+    R, C = 14336, 4096
+    x = I.weights(R, C, seed=2, device="cuda").float()
+    out = mx.mx_quantize_fp4_fp8(x, "floor", "both")
+    torch.cuda.synchronize()
+    for r0 in (0, 7168, R - 256):
+        exp = qat_oracle(x[r0:r0 + 256].cpu(), "floor")
+        b0 = r0 // 128
+        assert np.array_equal(out["fp4_codes"][r0:r0 + 256].cpu().numpy(), exp["fp4_codes"])
+        assert np.array_equal(out["fp4_scales"][r0:r0 + 256].cpu().numpy(), exp["fp4_scales"])
+        assert np.array_equal(out["e4m3"][r0:r0 + 256].cpu().numpy(), exp["e4m3"])
+        assert np.array_equal(out["block_scale"][b0:b0 + 2].cpu().numpy().view(np.uint32),
+                              exp["block_scale"].view(np.uint32))
+        assert np.array_equal(out["e4m3_t"][:, r0:r0 + 256].cpu().numpy(), exp["e4m3_t"])
