@@ -169,6 +169,43 @@ def summarize_counters_of(fetch_csv: str, write_csv: str, command: str, workload
     return "\n".join(lines) + "\n"
 
 
+# main kernel and element count of the workloads with SQ (instruction) counter summaries
+SQ_KERNELS = {
+    "activations": (CAST_KERNEL, ROWS * COLS),
+    "act_e2m3": ("mx_cast_kernel<true, 3, 0, 3, 0, false>", ROWS * COLS),
+    "grad_sr_e2m1": ("mx_cast_kernel<false, 2, 1, 2, 1, false>", 8192 * 8192),
+}
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+               "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR")
+
+
+def summarize_sq(command: str, csvs: list) -> str:
+    """Instruction counters per dispatch of each workload's main kernel, from
+    rocprofv3 --pmc runs of the SQ_COUNTERS (one CSV per workload, named
+    .../sq_<workload>/...). VALU lane-ops per element = SQ_INSTS_VALU * 64 / elements."""
+    out = ["# rocprofv3 instruction counters: VALU work per element and LDS bank conflicts", "",
+           f"command (per workload W): {command}", "",
+           "| workload | kernel | waves | VALU instr per wave | VALU lane-ops per element | SALU per wave | "
+           "LDS instr per wave | LDS bank-conflict cycles per LDS instr |", "|---|---|---|---|---|---|---|---|"]
+    for path in csvs:
+        w = next(k for k in SQ_KERNELS if f"sq_{k}" in path)
+        sub_, n = SQ_KERNELS[w]
+        m = _counter_means_all(path, sub_)
+        waves = m["SQ_WAVES"]
+        out.append(f"| {w} | {sub_} | {waves:.0f} | {m['SQ_INSTS_VALU'] / waves:.1f} | "
+                   f"{m['SQ_INSTS_VALU'] * 64 / n:.2f} | {m['SQ_INSTS_SALU'] / waves:.1f} | "
+                   f"{m['SQ_INSTS_LDS'] / waves:.1f} | {m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_INSTS_LDS'], 1):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_means_all(path, kernel_sub):
+    acc = {}
+    for r in _csv_rows(path):
+        if kernel_sub in r["Kernel_Name"]:
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     """HBM bytes per launch of the cast from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for torch's copy kernel
@@ -453,12 +490,17 @@ def main() -> int:
                     help="print a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the calibrated HBM-traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="COUNTER_CSV",
+                    help="print the VALU / LDS instruction-counter summary of rocprofv3 --pmc runs and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--trace-workload", default="activations", choices=sorted(TRACE_KERNELS),
                     help="which workload's kernels --summarize-trace / --summarize-counters report")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.command, args.trace_workload), end="")
+        return 0
+    if args.summarize_sq:
+        print(summarize_sq(args.command, args.summarize_sq), end="")
         return 0
     if args.summarize_counters:
         if args.trace_workload == "activations":

@@ -21,11 +21,15 @@
 // encoded with scale 1: the gfx950 conversions are exact and round to
 // nearest-even.
 //
+// The same kernel runs the quantization-aware step from master weights
+// (BF16 / FP32): each 1x32 sub-block is first cast to MXFP4 with the MX cast's
+// rules (and optionally stored as such), then goes through the steps above.
+//
 // One workgroup of 4 waves owns a 128-row x 256-column tile: two FP8 blocks
 // side by side. Thread t = 16 g + h holds rows 8g .. 8g+7 of half sub-block h
 // (16 codes: 8 bytes in, 16 bytes out), so 16 lanes cover a row and every
-// load and store instruction moves whole 128-byte lines (4 rows of 128 bytes
-// in, 4 rows of 256 bytes out). The transposed copy is staged as
+// MXFP4 load and FP8 store instruction moves whole 128-byte lines (4 rows of
+// 128 bytes in, 4 rows of 256 bytes out). The transposed copy is staged as
 // [column][row] bytes in LDS: each thread's 8 rows of a column are one 8-byte
 // slot, slot g of column c stored at slot g ^ (c / 16) (conflict-free for a
 // quarter wave), and leaves as 128-byte runs of the [C][R] plane.
