@@ -14,7 +14,9 @@ read once, each code and scale byte written once: 272,629,760 B per step).
 `roofline` compares that rate with MI355X's 8 TB/s HBM peak; `traffic`
 carries the HBM bytes per launch that rocprofv3 counters measured for the same
 kernel source (profiles/), or null if the kernel changed since. `cpu_baseline`
-times the CPU oracle on a bounded slab of the same tensor.
+times the CPU oracle, single-threaded, on a bounded slab of the same tensor;
+`cpu_baseline_parallel` times it over the whole tensor in up to 16 forked
+processes.
 """
 from __future__ import annotations
 
@@ -258,6 +260,47 @@ def cpu_baseline(x_gpu, budget_s: float = 12.0):
                       f"E4M3 floor, NumPy float64 oracle, single thread, {t_used:.1f} s"}
 
 
+_PAR_BITS = None
+
+
+def _oracle_slab(r0):
+    """Worker of cpu_baseline_parallel: the oracle on rows r0 .. r0+511 of the
+    host copy made before the workers were forked."""
+    import oracle as O
+    O.quantize(_PAR_BITS[r0:r0 + 512], "bf16", O.E4M3, O.FLOOR, O.BOTH)
+    return r0
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_parallel(x_gpu, procs: int):
+    """The same oracle over the whole tensor, in `procs` forked worker processes
+    taking disjoint 512-row slabs (the workers touch only host memory)."""
+    import multiprocessing as mp
+    import mx_inputs as I
+    global _PAR_BITS
+    _PAR_BITS = I.to_bits(x_gpu)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        pool.map(_oracle_slab, [0])                     # start the workers
+        t0 = time.perf_counter()
+        pool.map(_oracle_slab, range(0, ROWS, 512), chunksize=1)
+        t = time.perf_counter() - t0
+    _PAR_BITS = None
+    return {"value": round(ALG_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"all {ROWS} rows in 512-row slabs over {procs} processes, fused row+col E4M3 floor, "
+                      f"NumPy float64 oracle, {t:.2f} s; CPU {_cpu_model()}"}
+
+
 CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4, "e2m3": 6, "e3m2": 6, "int8": 8}
 
 
@@ -483,6 +526,8 @@ def main() -> int:
                     help="rotating input/output buffer sets (default per workload: 8; 16 for the "
                          "requantization; 1 for the 30 GB wide-range batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="worker processes of the parallel oracle baseline (0: skip it); capped at the host's cores")
     ap.add_argument("--workload", default="activations", choices=sorted(WORKLOADS),
                     help="activations (default) is the fused row+col MXFP8 cast the metric is quoted on; "
                          "the others time the remaining workloads the same way")
@@ -594,7 +639,11 @@ def main() -> int:
     }
     if not args.no_cpu_baseline and args.workload == "activations":
         import mx_inputs as I
-        line["cpu_baseline"] = cpu_baseline(I.activations(ROWS, COLS, seed=1, device=dev))
+        xa = I.activations(ROWS, COLS, seed=1, device=dev)
+        line["cpu_baseline"] = cpu_baseline(xa)
+        procs = min(args.cpu_procs, os.cpu_count() or 1)
+        if procs > 1:
+            line["cpu_baseline_parallel"] = cpu_baseline_parallel(xa, procs)
     print(json.dumps(line))
     return 0
 
