@@ -594,6 +594,17 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     alg_bytes = wl["bytes"]
+
+    # spread of single steps (outside the timed region): 64 steps, each between its own events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        steps_fns[i % args.sets]()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    one = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    per_launch = {"p10": round(one[6], 2), "p50": round(one[32], 2), "p90": round(one[57], 2), "unit": "us",
+                  "samples": len(one)}
     del steps_fns
     torch.cuda.empty_cache()
 
@@ -631,6 +642,7 @@ def main() -> int:
         "data": "synthetic",
         "config": dict(wl["config"], buffer_sets=args.sets, alg_bytes_per_step=alg_bytes),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "per_launch_us": per_launch,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "copy_ceiling": {"value": round(copy_gbs, 2), "unit": "GB/s",
