@@ -96,6 +96,15 @@ TRACE_KERNELS = {
                    ("nv_cast_kernel<true, 3>", "nv_cast_kernel<bf16,row+col>",
                     _NV_N * 2 + 2 * (_NV_N // 2 + _NV_N // 16)),
                    ("nv_zero_kernel", "nv_zero_kernel (clears g)", 4)]),
+    "act_e2m3": ("fused MXFP6 E2M3 row+col cast, 16384x4096 BF16",
+                 [("mx_cast_kernel<true, 3, 0, 3, 0, false>", "mx_cast_kernel<bf16,E2M3,floor,row+col>",
+                   _NV_N * 2 + 2 * (_NV_N * 3 // 4 + _NV_N // 32))]),
+    "act_int8": ("fused MXINT8 row+col cast, 16384x4096 BF16",
+                 [("mx_cast_kernel<true, 5, 0, 3, 0, false>", "mx_cast_kernel<bf16,INT8,floor,row+col>",
+                   _NV_N * 2 + 2 * (_NV_N + _NV_N // 32))]),
+    "weights_2d_e2m1": ("MXFP4 E2M1 32x32-block row+col cast, 14336x4096 BF16",
+                        [("mx_cast_kernel<true, 2, 0, 3, 0, true>", "mx_cast_kernel<bf16,E2M1,floor,row+col,32x32>",
+                          _RQ_N * 2 + 2 * (_RQ_N // 2 + _RQ_N // 1024))]),
     "weights_fp4_in_fp8": ("MXFP4 -> FP8 128x128 requantization, row + transposed copy + spreads, 14336x4096",
                            [("requant_kernel<true, true>", "requant_kernel<row+col>",
                              _RQ_N // 2 + _RQ_N // 32 + 2 * (_RQ_N + 4 * (_RQ_N // 16384)) + _RQ_N // 16384)]),
@@ -127,6 +136,12 @@ def summarize_trace(stats_csv: str, command: str, workload: str = "activations")
 # per workload, for the counter summaries: (kernel-name substring, short name,
 # algorithmic bytes read, algorithmic bytes written) per launch
 COUNTER_KERNELS = {
+    "act_e2m3": [("mx_cast_kernel<true, 3, 0, 3, 0, false>", "mx_cast_kernel<bf16,E2M3,floor,row+col>", _NV_N * 2,
+                  2 * (_NV_N * 3 // 4 + _NV_N // 32))],
+    "act_int8": [("mx_cast_kernel<true, 5, 0, 3, 0, false>", "mx_cast_kernel<bf16,INT8,floor,row+col>", _NV_N * 2,
+                  2 * (_NV_N + _NV_N // 32))],
+    "weights_2d_e2m1": [("mx_cast_kernel<true, 2, 0, 3, 0, true>", "mx_cast_kernel<bf16,E2M1,floor,row+col,32x32>",
+                         _RQ_N * 2, 2 * (_RQ_N // 2 + _RQ_N // 1024))],
     "act_nvfp4": [("nv_amax_kernel<true>", "nv_amax_kernel<bf16>", _NV_N * 2, 0),
                   ("nv_cast_kernel<true, 3>", "nv_cast_kernel<bf16,row+col>", _NV_N * 2, 2 * (_NV_N // 2 + _NV_N // 16))],
     "weights_fp4_in_fp8": [("requant_kernel<true, true>", "requant_kernel<row+col>", _RQ_N // 2 + _RQ_N // 32,
