@@ -36,6 +36,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "GB/s (read+write) and % of HBM peak, MXFP8 row+col cast 16384×4096"
 COUNTERS = os.path.join(ROOT, "profiles", "fused_cast_e4m3_16384x4096_counters.txt")
 KERNEL_SOURCES = ["microscaling_block_quantized_amd/csrc/mx_cast.hip",
+                  "microscaling_block_quantized_amd/csrc/mx_api.cpp",
+                  "microscaling_block_quantized_amd/csrc/mx_kernels.h",
                   "microscaling_block_quantized_amd/csrc/mx_cast_impl.h",
                   "microscaling_block_quantized_amd/csrc/mx_sr.h",
                   "microscaling_block_quantized_amd/csrc/mx_device.h"]

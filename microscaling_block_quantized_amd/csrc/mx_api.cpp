@@ -145,6 +145,12 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
   // 32x32 blocks, of 128 columns in one row of the scale grid (same condition)
   if (want_row && aligned(row_scales, 4) && (row_stream || s.cols % 128 == 0)) a.flags |= mx::kRowScaleDword;
   if (want_col && s.rows % 128 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
+  // Column-plane pitches that are multiples of 4 KiB: stagger the XCD strips so the
+  // transposed stores in flight spread over the HBM channels. Measured on MI355X:
+  // 16384-row 8-bit planes 4-7% faster; pitches like 14 KiB, tensors of fewer
+  // than 64 tile rows and the 6-bit planes (ordinary stores) slightly slower.
+  if (want_col && code_bits(fmt) != 6 && (s.rows * code_bits(fmt) / 8) % 4096 == 0 && g.tiles_r >= 64)
+    a.flags |= mx::kStaggerStrips;
   const bool bf = x_dtype == MX_BF16;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const uint32_t nb = uint32_t(g.blocks);

@@ -91,8 +91,15 @@ __device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
 // tile sequence that is ordered strip-major: tile columns are cut into 8
 // strips, and each strip is walked batch by batch, row by row. Neighbouring
 // tiles of one strip then run at the same time on the same XCD.
+//
+// stagger: strip s starts its walk s * (rows_total / 16) tile rows further
+// down (wrapping). All strips advance at about the same pace, so without it
+// every column-plane store in flight lands in the same few KiB of its
+// transposed row; when that row's pitch is a multiple of 4 KiB those stores
+// share address bits and crowd a subset of the HBM channels. The rotation is
+// a permutation of each strip's tiles, so every tile is still visited once.
 __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nb, uint32_t tiles_r, uint32_t tiles_c,
-                                            uint32_t& b, uint32_t& tr, uint32_t& tc) {
+                                            bool stagger, uint32_t& b, uint32_t& tr, uint32_t& tc) {
   const uint32_t xcd = bid % kXcds, idx = bid / kXcds;
   const uint32_t per = nb / kXcds, rem = nb % kXcds;
   const uint32_t i = xcd * per + min(xcd, rem) + idx;                // position in the sequence
@@ -101,8 +108,11 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nb, uint32_t 
   const uint32_t strip = i / (rows_total * w);
   const uint32_t in = i - strip * rows_total * w;
   const uint32_t ws = min(w, tiles_c - strip * w);
-  const uint32_t rowi = in / ws;
-  tc = strip * w + (in - rowi * ws);
+  const uint32_t rowi0 = in / ws;
+  tc = strip * w + (in - rowi0 * ws);
+  // strip <= 7, so the rotated index stays below 2 * rows_total
+  const uint32_t rot = rowi0 + (stagger ? strip * max(1u, rows_total / 16u) : 0u);
+  const uint32_t rowi = rot >= rows_total ? rot - rows_total : rot;
   b = rowi / tiles_r;
   tr = rowi - b * tiles_r;
 }
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * kWaveRows : 4];
 
   uint32_t bi, tr, tcol;
-  tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, bi, tr, tcol);
+  tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, (a.flags & kStaggerStrips) != 0, bi, tr, tcol);
   const int64_t R = a.rows, C = a.cols;
   const int64_t r0 = int64_t(tr) * kTileR;
   const int64_t c0 = int64_t(tcol) * kTileC;

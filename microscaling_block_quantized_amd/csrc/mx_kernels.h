@@ -17,7 +17,7 @@ struct CastArgs {
   int64_t rows, cols;     // per batch slice
   int64_t elements;       // batch * rows * cols
   uint32_t tiles_r, tiles_c;
-  uint32_t flags;         // kRowScaleDword / kColScaleDword
+  uint32_t flags;         // kRowScaleDword / kColScaleDword / kStaggerStrips
   uint32_t seed_lo, seed_hi;   // Philox key of stochastic rounding
 };
 
@@ -27,6 +27,9 @@ struct CastArgs {
 constexpr uint32_t kRowScaleDword = 1u;
 constexpr uint32_t kColScaleDword = 2u;
 constexpr uint32_t kNvMarkedAmax = 4u;   // NVFP4 cast: global_scale holds marked maxima
+// Tiled MX cast: rotate each XCD strip's walk over the tile rows (tile_coords).
+// Set by the host when the column plane's pitch is a multiple of 4 KiB.
+constexpr uint32_t kStaggerStrips = 8u;
 
 struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;

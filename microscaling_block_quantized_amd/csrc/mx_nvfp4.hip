@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   __shared__ float lds_rtab[kNvTab];
 
   uint32_t bi, tr, tcol;
-  tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, bi, tr, tcol);
+  tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, false, bi, tr, tcol);
   const int64_t R = a.rows, C = a.cols;
   const int64_t r0 = int64_t(tr) * kTileR;
   const int64_t c0 = int64_t(tcol) * kTileC;

@@ -160,6 +160,33 @@ def test_ragged_shapes(mx, fmt, dt):
             check(mx, x, fmt, mode, axis, f"ragged {(b, r, c, axis, mode)}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "int8"])
+def test_staggered_strip_order(mx, fmt, dt):
+    """8192-row slices give column-plane pitches of 8 or 4 KiB and 64 tile rows,
+    where the tiled kernel rotates each XCD strip's walk over the tile rows.
+    Two slices (the rotation runs over both) and 288 columns (two tile columns,
+    the second ragged). Outputs start as a sentinel, so a tile the walk skipped
+    or visited twice with another tile's coordinates shows up."""
+    g = torch.Generator().manual_seed(23)
+    b, r, c = 2, 8192, 288
+    x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-6, 6, (b, r // 32, 1, 1), generator=g)
+                                                        .float()).expand(b, r // 32, 32, 1).reshape(b, r, 1)
+    x = x.to(torch.bfloat16) if dt == "bf16" else x
+    bits = {"e4m3": 8, "e2m1": 4, "int8": 8}[fmt]
+    for axis in ("both", "col"):
+        out = {}
+        if axis == "both":
+            out["row_codes"] = torch.full((b, r, c * bits // 8), 0xA5, dtype=torch.uint8, device="cuda")
+            out["row_scales"] = torch.full((b, r, c // 32), 0xA5, dtype=torch.uint8, device="cuda")
+        out["col_codes"] = torch.full((b, c, r * bits // 8), 0xA5, dtype=torch.uint8, device="cuda")
+        out["col_scales"] = torch.full((b, c, r // 32), 0xA5, dtype=torch.uint8, device="cuda")
+        got = mx.mx_quantize(x.cuda(), fmt, "floor", axis, out=out)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in got.items()}
+        assert_same(got, oracle_quant(x, fmt, "floor", axis), f"staggered {(b, r, c, fmt, dt, axis)}")
+
+
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("fmt", NEW_FMTS)
 def test_new_formats_workloads(mx, fmt, mode):
