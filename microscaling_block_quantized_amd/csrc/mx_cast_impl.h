@@ -83,6 +83,14 @@ __device__ __forceinline__ void store12(void* p, uint32_t a, uint32_t b, uint32_
   q[1] = b;
   q[2] = c;
 }
+// A dword store with the agent-scope bit (sc1). Used for the row-scale plane of
+// the 6-bit formats, whose ordinary code stores keep L2 full of dirty partial
+// lines: there it measured 1.5-3% faster on MI355X than a plain store. With the
+// non-temporal code planes of the other formats it measured 6% slower. (A 4-byte
+// store has no data hazard with the next VALU write, so no wait state is due.)
+__device__ __forceinline__ void store_sc1_4(void* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 __device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
   __builtin_nontemporal_store(static_cast<unsigned short>(v), reinterpret_cast<unsigned short*>(p));
 }
@@ -352,7 +360,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if (!B2 && t < RPT && lrow + t < rows_in && 128 * wc < cols_in) {
       uint8_t* dst = a.row_scales + tile_elem / 32 + (uint32_t(lrow + t) * Cu + uint32_t(128 * wc)) / 32;
       if (a.flags & kRowScaleDword) {
-        *reinterpret_cast<uint32_t*>(dst) = scale_dw;
+        if constexpr (CB == 6) store_sc1_4(dst, scale_dw);
+        else *reinterpret_cast<uint32_t*>(dst) = scale_dw;
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
