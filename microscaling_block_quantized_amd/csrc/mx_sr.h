@@ -127,12 +127,15 @@ __device__ __forceinline__ float sr_scaled_flat(uint32_t xb, int e, uint32_t u) 
   return __uint_as_float(r);
 }
 
-// The same for every input but FP32 subnormals, with fewer operations: x
-// zero, saturating, or normal. A normal x below saturation has d >= 17 (the
-// spacing is at least 2^(23 - mbits) of its ulps; INT8: 2^17), so the
-// d <= 0 case and the leading-zero count of sr_scaled_flat drop out. Sets
-// `slow` for a subnormal x, and the caller then recomputes with
-// sr_scaled_flat.
+// The same decision through the FP32 pipeline, for every input but FP32
+// subnormals and the tiniest elements of a block. With eq the exponent of the
+// grid spacing at |x| (as above), y = |x| / 2^eq is exact while it is a normal
+// number, and so are n = floor(y) and the fraction y - n. The rule "fraction
+// > u / 2^16" is then the exact comparison fraction * 2^16 > u, both sides
+// exact in FP32, and (n or n + 1) * 2^(eq - e) is the exact grid value. Sets
+// `slow` for an FP32-subnormal x (whose exponent field does not give
+// floor(log2 |x|)) and for a y below 2^-126. The caller then recomputes with
+// sr_scaled_flat. Zero needs no case of its own: y = 0 never rounds up.
 template <int F>
 __device__ __forceinline__ float sr_scaled_fast(uint32_t xb, int e, float lim, uint32_t u, bool& slow) {
   const uint32_t ab = xb & 0x7FFFFFFFu;
@@ -140,19 +143,14 @@ __device__ __forceinline__ float sr_scaled_fast(uint32_t xb, int e, float lim, u
   int eq;
   if constexpr (F == kInt8) eq = e - 6;
   else eq = max(field - 127, e + SrC<F>::emin) - SrC<F>::mbits;
-  const int d = eq - field + 150;
-  const uint32_t mant = (ab & 0x7FFFFFu) | 0x800000u;
-  const uint32_t n = mant >> uint32_t(min(max(d, 0), 31));
-  const uint32_t sh = uint32_t(min(max(d - 32, 0), 24));
-  const uint32_t rem = d <= 32 ? mant << uint32_t((32 - d) & 31) : mant >> sh;
-  const bool lost = d > 32 && (mant & ((1u << sh) - 1u)) != 0u;
-  const uint32_t thr = u << 16;
-  const bool up = rem > thr || (rem == thr && lost);
-  const float v = float(n + (up ? 1u : 0u)) * __uint_as_float(uint32_t(eq - e + 127) << 23);
+  const float y = __builtin_ldexpf(__uint_as_float(ab), -eq);
+  const float n = __builtin_floorf(y);
+  const bool up = (y - n) * 65536.0f > float(u);
+  const float v = __builtin_ldexpf(up ? n + 1.0f : n, eq - e);
+  slow |= (field == 0 || y < 0x1p-126f) && ab != 0u;
   const bool sat = !(__uint_as_float(ab) < lim);
-  slow |= field == 0 && ab != 0u;
   const uint32_t mag = sat ? __float_as_uint(SrC<F>::vmax) : __float_as_uint(v);
-  return __uint_as_float(ab == 0u ? xb : ((xb & 0x80000000u) | mag));
+  return __uint_as_float((xb & 0x80000000u) | mag);
 }
 
 // N elements. FAST: through the fast path, redone with sr_scaled_flat when any
