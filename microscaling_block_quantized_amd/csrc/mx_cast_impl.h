@@ -152,6 +152,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
   __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * kWaveRows : 4];
+  // 4-bit codes with both copies: a wave row's row codes are only 64 bytes, half
+  // of a 128-byte line whose other half comes from the neighbouring wave. They are
+  // staged here as [tile row][128 bytes] and, after the barrier the column copy
+  // needs anyway, written out as whole lines.
+  constexpr bool ROWLDS = ROWS && COLS && CB == 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_rows[ROWLDS ? kTileR * kTileC / 2 : 16];
+  // byte offset of (tile row r, tile column c) in lds_rows: the 16-byte chunk index
+  // XORed with (r / 8) mod 8, so that the 4 row groups of a wave hit different banks
+  auto rows_off = [](int r, int c) { return r * (kTileC / 2) + ((c / 2) ^ (((r >> 3) & 7) << 4)); };
 
   uint32_t bi, tr, tcol;
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, (a.flags & kStaggerStrips) != 0, bi, tr, tcol);
@@ -299,6 +308,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           const uint32_t e0 = pack6(w.x) | (hi << 24), e1 = hi >> 8;
           const uint32_t o0 = dpp<kDppXor1>(e0), o1 = dpp<kDppXor1>(e1);
           if (ok && (t & 1) == 0) store12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+        } else if constexpr (ROWLDS) {
+          *reinterpret_cast<uint32_t*>(lds_rows + rows_off(lrow + k, lcol)) = w.x;
         } else if (ok) {
           if constexpr (CB == 8) store_nt8(dst, w);
           else store_nt4(dst, w.x);
@@ -317,6 +328,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           const uint32_t g0 = pack6(w);
           const uint32_t g1 = dpp<kDppQuadNext>(g0), g2 = dpp<kDppXor2>(g0), g3 = dpp<kDppQuadPrev>(g0);
           if (ok && (t & 3) == 0) store12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+        } else if constexpr (ROWLDS) {
+          *reinterpret_cast<uint16_t*>(lds_rows + rows_off(lrow + k, lcol)) = uint16_t(w);
         } else if (ok) {
           if constexpr (CB == 8) store_nt4(dst, w);
           else store_nt2(dst, w);
@@ -474,6 +487,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           store12(dst, p.x, p.y, p.z);
         } else {
           store_nt16(dst, w);
+        }
+      }
+    }
+    if constexpr (ROWLDS) {
+      // the staged row codes: 8 lanes write one tile row's 128 bytes (256 columns)
+      uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem / 2;
+#pragma unroll
+      for (int i = 0; i < kTileR * 8 / kThreads; ++i) {
+        const int id = threadIdx.x + i * kThreads;
+        const int rl = id >> 3, part = id & 7;
+        if (rl < rows_in && 32 * part < cols_in) {
+          const uint4 w = *reinterpret_cast<const uint4*>(lds_rows + rl * (kTileC / 2) + ((part ^ ((rl >> 3) & 7)) << 4));
+          store_nt16(rct + uint32_t(rl) * (Cu / 2) + uint32_t(16 * part), w);
         }
       }
     }
