@@ -210,6 +210,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
   __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * SPC : 4];
   __shared__ float lds_rtab[kNvTab];
+  // With both copies, a wave row's row codes (64 bytes, half of a 128-byte line) are
+  // staged as [tile row][128 bytes] and written as whole lines after the barrier the
+  // column copy needs anyway; chunk index XORed with (row / 8) mod 8 against bank
+  // conflicts between the row groups of a wave.
+  constexpr bool ROWLDS = ROWS && COLS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_rows[ROWLDS ? kTileR * kTileC / 2 : 16];
+  auto rows_off = [](int r, int c) { return r * (kTileC / 2) + ((c / 2) ^ (((r >> 3) & 7) << 4)); };
 
   uint32_t bi, tr, tcol;
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, false, bi, tr, tcol);
@@ -313,10 +320,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       if constexpr (BF16) {
         const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk) |
                            (nv_encode4(elem(k, 4), elem(k, 5), elem(k, 6), elem(k, 7), blk) << 16);
-        if (ok) store_nt4(dst, w);
+        if constexpr (ROWLDS) *reinterpret_cast<uint32_t*>(lds_rows + rows_off(lrow + k, lcol)) = w;
+        else if (ok) store_nt4(dst, w);
       } else {
         const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk);
-        if (ok) store_nt2(dst, w);
+        if constexpr (ROWLDS) *reinterpret_cast<uint16_t*>(lds_rows + rows_off(lrow + k, lcol)) = uint16_t(w);
+        else if (ok) store_nt2(dst, w);
       }
       // OR the codes of the 4 blocks of each group of HALF lanes into one dword that every
       // lane of the group holds: BF16 pairs lanes 2 apart (quad_perm), then the two halves
@@ -387,6 +396,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         } else {                                       // rows of R/2 bytes are only 8-byte aligned
           store_nt8(dst, make_uint2(w.x, w.y));
           store_nt8(dst + 8, make_uint2(w.z, w.w));
+        }
+      }
+    }
+    if constexpr (ROWLDS) {
+      // the staged row codes: 8 lanes per tile row, 16 bytes (32 columns) each; a
+      // ragged last chunk holds 16 columns, and rows of C/2 bytes with C % 32 != 0
+      // are only 8-byte aligned
+      uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem / 2;
+#pragma unroll
+      for (int i = 0; i < kTileR * 8 / kThreads; ++i) {
+        const int id = threadIdx.x + i * kThreads;
+        const int rl = id >> 3, part = id & 7;
+        if (rl < rows_in && 32 * part < cols_in) {
+          const uint4 w = *reinterpret_cast<const uint4*>(lds_rows + rl * (kTileC / 2) + ((part ^ ((rl >> 3) & 7)) << 4));
+          uint8_t* dst = rct + uint32_t(rl) * (Cu / 2) + uint32_t(16 * part);
+          if (32 * part + 32 > cols_in) {
+            store_nt8(dst, make_uint2(w.x, w.y));
+          } else if (Cu % 32 == 0) {
+            store_nt16(dst, w);
+          } else {
+            store_nt8(dst, make_uint2(w.x, w.y));
+            store_nt8(dst + 8, make_uint2(w.z, w.w));
+          }
         }
       }
     }
