@@ -161,6 +161,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // byte offset of (tile row r, tile column c) in lds_rows: the 16-byte chunk index
   // XORed with (r / 8) mod 8, so that the 4 row groups of a wave hit different banks
   auto rows_off = [](int r, int c) { return r * (kTileC / 2) + ((c / 2) ^ (((r >> 3) & 7) << 4)); };
+  // 6-bit codes from BF16 with both copies: a wave row's 96 bytes, stored 12 at
+  // a time by half the lanes, straddle lines. They are staged as [tile row][192
+  // bytes] (row pitch padded by 16 bytes against bank conflicts between row
+  // groups) and written as 16-byte chunks, all lanes busy, when the row-plane
+  // pitch 3C/4 is a multiple of 16 bytes (cols % 64 == 0); otherwise directly.
+  // (The FP32 kernel, at one workgroup per CU, measured slower staged.)
+  constexpr bool ROWLDS6 = ROWS && COLS && CB == 6 && BF16;
+  constexpr int P6 = kTileC * 6 / 8 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_rows6[ROWLDS6 ? kTileR * P6 : 16];
 
   uint32_t bi, tr, tcol;
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, (a.flags & kStaggerStrips) != 0, bi, tr, tcol);
@@ -171,6 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int rows_in = int(min<int64_t>(R - r0, kTileR));
   const int cols_in = int(min<int64_t>(C - c0, kTileC));
   const uint32_t Cu = uint32_t(C);             // host guarantees C < 2^22 and, for columns, R < 2^23
+  const bool lines6 = ROWLDS6 && (Cu & 63u) == 0u;
 
   const int wid = threadIdx.x >> 6;
   const int wr = wid % kWaveRows, wc = wid / kWaveRows;
@@ -307,7 +317,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           const uint32_t hi = pack6(w.y);
           const uint32_t e0 = pack6(w.x) | (hi << 24), e1 = hi >> 8;
           const uint32_t o0 = dpp<kDppXor1>(e0), o1 = dpp<kDppXor1>(e1);
-          if (ok && (t & 1) == 0) store12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+          if (lines6) {
+            if ((t & 1) == 0) {
+              uint32_t* l = reinterpret_cast<uint32_t*>(lds_rows6 + (lrow + k) * P6 + (96 * wc + 6 * t));
+              l[0] = e0;
+              l[1] = e1 | (o0 << 16);
+              l[2] = (o0 >> 16) | (o1 << 16);
+            }
+          } else if (ok && (t & 1) == 0) {
+            store12(dst, e0, e1 | (o0 << 16), (o0 >> 16) | (o1 << 16));
+          }
         } else if constexpr (ROWLDS) {
           *reinterpret_cast<uint32_t*>(lds_rows + rows_off(lrow + k, lcol)) = w.x;
         } else if (ok) {
@@ -327,7 +346,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           // 24 bits per lane: lane 4i stores the 12 bytes of lanes 4i .. 4i+3
           const uint32_t g0 = pack6(w);
           const uint32_t g1 = dpp<kDppQuadNext>(g0), g2 = dpp<kDppXor2>(g0), g3 = dpp<kDppQuadPrev>(g0);
-          if (ok && (t & 3) == 0) store12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+          if (lines6) {
+            if ((t & 3) == 0) {
+              uint32_t* l = reinterpret_cast<uint32_t*>(lds_rows6 + (lrow + k) * P6 + (96 * wc + 3 * t));
+              l[0] = g0 | (g1 << 24);
+              l[1] = (g1 >> 8) | (g2 << 16);
+              l[2] = (g2 >> 16) | (g3 << 8);
+            }
+          } else if (ok && (t & 3) == 0) {
+            store12(dst, g0 | (g1 << 24), (g1 >> 8) | (g2 << 16), (g2 >> 16) | (g3 << 8));
+          }
         } else if constexpr (ROWLDS) {
           *reinterpret_cast<uint16_t*>(lds_rows + rows_off(lrow + k, lcol)) = uint16_t(w);
         } else if (ok) {
@@ -487,6 +515,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           store12(dst, p.x, p.y, p.z);
         } else {
           store_nt16(dst, w);
+        }
+      }
+    }
+    if (lines6) {
+      // the staged 6-bit row codes: 12 chunks of 16 bytes per tile row, through L2
+      // (lines at the tile's edges are shared with the neighbouring tile); a
+      // ragged tile's last chunk may hold 8 valid bytes
+      uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem * 6 / 8;
+      const uint32_t rpitch = Cu * 6 / 8;
+      const int bytes_in = cols_in * 6 / 8;
+#pragma unroll
+      for (int i = 0; i < kTileR * 12 / kThreads; ++i) {
+        const int id = threadIdx.x + i * kThreads;
+        const int rl = id / 12, part = id % 12;
+        if (rl < rows_in && 16 * part < bytes_in) {
+          const uint4 w = *reinterpret_cast<const uint4*>(lds_rows6 + rl * P6 + 16 * part);
+          uint8_t* dst = rct + uint32_t(rl) * rpitch + uint32_t(16 * part);
+          if (16 * part + 16 <= bytes_in) *reinterpret_cast<uint4*>(dst) = w;
+          else *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
         }
       }
     }

@@ -161,6 +161,28 @@ def test_ragged_shapes(mx, fmt, dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_row_lines(mx, fmt, dt):
+    """Fused 6-bit casts with cols % 64 == 0 stage the row codes and write them
+    as 16-byte chunks: tiles of 256, 64 and 192 columns (ragged last tiles), a
+    batch, and outputs that start as a sentinel so that a chunk left unwritten
+    shows up."""
+    g = torch.Generator().manual_seed(29)
+    for b, r, c in [(2, 96, 320), (1, 64, 64), (1, 128, 4160), (3, 32, 448)]:
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-8, 8, (b, r, 1), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
+        out = {"row_codes": torch.full((b, r, c * 3 // 4), 0xA5, dtype=torch.uint8, device="cuda"),
+               "row_scales": torch.full((b, r, c // 32), 0xA5, dtype=torch.uint8, device="cuda"),
+               "col_codes": torch.full((b, c, r * 3 // 4), 0xA5, dtype=torch.uint8, device="cuda"),
+               "col_scales": torch.full((b, c, r // 32), 0xA5, dtype=torch.uint8, device="cuda")}
+        for mode in MODES:
+            got = mx.mx_quantize(x.cuda(), fmt, mode, "both", out=out)
+            torch.cuda.synchronize()
+            got = {k: v.cpu().numpy() for k, v in got.items()}
+            assert_same(got, oracle_quant(x, fmt, mode, "both"), f"fp6 lines {(b, r, c, fmt, dt, mode)}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "int8"])
 def test_staggered_strip_order(mx, fmt, dt):
     """8192-row slices give column-plane pitches of 8 or 4 KiB and 64 tile rows,
