@@ -244,6 +244,36 @@ __device__ __forceinline__ uint32_t int8_encode4(float f0, float f1, float f2, f
   return code == 0xFFu ? FmtC<kInt8>::nan_fill : w;
 }
 
+// Four BF16 pairs straight from their bits, for block codes >= 8. A BF16 dot
+// product with one zero weight gives x * 2^(133 - code) exactly (a BF16 value
+// times a power of two that BF16 holds), and adding the magic constant rounds
+// once to the nearest integer, as the FMA in int8_bits does. For code >= 8, a
+// subnormal input scales below 0.5 and gives 0 whether or not the unit flushes
+// it. An Inf or NaN partner in the other half of a pair poisons the sum, but
+// such a block has code 0xFF and is overwritten.
+__device__ __forceinline__ uint32_t int8_from_dot(uint32_t p, uint32_t wbits) {
+  const float r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, wbits),
+                                                  kMagic, false);
+  const int b = int(__float_as_uint(r));
+  return uint32_t(min(max(b, kMagicBits - 127), kMagicBits + 127));
+}
+__device__ __forceinline__ uint2 int8_encode8_bf16(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
+                                                   uint32_t code) {
+  // a block code below 8 anywhere in the wave (block max < 2^-119) takes the
+  // general path for the whole wave
+  if (__builtin_amdgcn_ballot_w64(code < 8u) != 0) {
+    return make_uint2(int8_encode4(bf16_lo(p0), bf16_hi(p0), bf16_lo(p1), bf16_hi(p1), code),
+                      int8_encode4(bf16_lo(p2), bf16_hi(p2), bf16_lo(p3), bf16_hi(p3), code));
+  }
+  const uint32_t mb = (260u - code) << 7;              // 2^(133 - code) as BF16 bits
+  const uint32_t wl = mb, wh = mb << 16;               // weights (m, 0) and (0, m)
+  const uint32_t x = pack_low_bytes(int8_from_dot(p0, wl), int8_from_dot(p0, wh), int8_from_dot(p1, wl),
+                                    int8_from_dot(p1, wh));
+  const uint32_t y = pack_low_bytes(int8_from_dot(p2, wl), int8_from_dot(p2, wh), int8_from_dot(p3, wl),
+                                    int8_from_dot(p3, wh));
+  return code == 0xFFu ? make_uint2(FmtC<kInt8>::nan_fill, FmtC<kInt8>::nan_fill) : make_uint2(x, y);
+}
+
 // Encode four BF16 pairs (p0..p3, element order p0.lo, p0.hi, p1.lo, ...).
 // FP8 / FP6 / INT8: 8 codes, one per byte, in two dwords. FP4: 8 codes in one
 // dword (.y unused).
@@ -256,8 +286,7 @@ __device__ __forceinline__ uint2 encode8_bf16(uint32_t p0, uint32_t p1, uint32_t
     r.x = fp6_encode4_bf16<F, M>(p0, p1, code);
     r.y = fp6_encode4_bf16<F, M>(p2, p3, code);
   } else if constexpr (F == kInt8) {
-    r.x = int8_encode4(bf16_lo(p0), bf16_hi(p0), bf16_lo(p1), bf16_hi(p1), code);
-    r.y = int8_encode4(bf16_lo(p2), bf16_hi(p2), bf16_lo(p3), bf16_hi(p3), code);
+    r = int8_encode8_bf16(p0, p1, p2, p3, code);
   } else if constexpr (F == kE2M1) {
     uint32_t w = cvt2_fp4_bf16<0>(0u, p0, sc);
     w = cvt2_fp4_bf16<1>(w, p1, sc);
