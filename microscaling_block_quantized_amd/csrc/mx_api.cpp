@@ -145,6 +145,7 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
   // 32x32 blocks, of 128 columns in one row of the scale grid (same condition)
   if (want_row && aligned(row_scales, 4) && (row_stream || s.cols % 128 == 0)) a.flags |= mx::kRowScaleDword;
   if (want_col && s.rows % 128 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
+  if (want_row && want_col && !b2d && s.cols % 256 == 0 && aligned(row_scales, 8)) a.flags |= mx::kRowScaleQword;
   // Column-plane pitches that are multiples of 4 KiB: stagger the XCD strips so the
   // transposed stores in flight spread over the HBM channels. Measured on MI355X:
   // 16384-row 8-bit planes 4-7% faster; pitches like 14 KiB, tensors of fewer

@@ -91,6 +91,11 @@ __device__ __forceinline__ void store12(void* p, uint32_t a, uint32_t b, uint32_
 __device__ __forceinline__ void store_sc1_4(void* p, uint32_t v) {
   asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
+// The same for 8 bytes (still no wait state due: the data hazard needs more than 8).
+__device__ __forceinline__ void store_sc1_8(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2 d = u32x2{lo, hi};
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(d) : "memory");
+}
 __device__ __forceinline__ void store_nt2(void* p, uint32_t v) {
   __builtin_nontemporal_store(static_cast<unsigned short>(v), reinterpret_cast<unsigned short*>(p));
 }
@@ -170,6 +175,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr bool ROWLDS6 = ROWS && COLS && CB == 6 && BF16;
   constexpr int P6 = kTileC * 6 / 8 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds_rows6[ROWLDS6 ? kTileR * P6 : 16];
+  // Row scales with both copies and full-width tiles (kRowScaleQword: cols % 256
+  // == 0, plane 8-byte aligned): the two waves' scale dwords of a tile row are
+  // staged and leave as one 8-byte store after the barrier. That halves the
+  // stores, and each tile's piece of a 128-byte scale line arrives in one
+  // transaction. Such a line is written by all 8 XCDs.
+  constexpr bool RS8 = ROWS && COLS && !B2;
+  __shared__ uint32_t lds_rs[RS8 ? kTileR * 2 : 1];
 
   uint32_t bi, tr, tcol;
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, (a.flags & kStaggerStrips) != 0, bi, tr, tcol);
@@ -181,6 +193,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int cols_in = int(min<int64_t>(C - c0, kTileC));
   const uint32_t Cu = uint32_t(C);             // host guarantees C < 2^22 and, for columns, R < 2^23
   const bool lines6 = ROWLDS6 && (Cu & 63u) == 0u;
+  const bool rs8 = RS8 && (a.flags & kRowScaleQword) != 0;
 
   const int wid = threadIdx.x >> 6;
   const int wr = wid % kWaveRows, wc = wid / kWaveRows;
@@ -398,7 +411,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
     // lane t < RPT stores the scale bytes of tile row lrow + t, wave columns 128*wc .. +127
-    if (!B2 && t < RPT && lrow + t < rows_in && 128 * wc < cols_in) {
+    // (or stages them for the 8-byte store after the barrier)
+    if (rs8) {
+      if (t < RPT) lds_rs[(lrow + t) * 2 + wc] = scale_dw;
+    } else if (!B2 && t < RPT && lrow + t < rows_in && 128 * wc < cols_in) {
       uint8_t* dst = a.row_scales + tile_elem / 32 + (uint32_t(lrow + t) * Cu + uint32_t(128 * wc)) / 32;
       if (a.flags & kRowScaleDword) {
         if constexpr (CB == 6) store_sc1_4(dst, scale_dw);
@@ -517,6 +533,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           store_nt16(dst, w);
         }
       }
+    }
+    if (rs8 && int(threadIdx.x) < rows_in) {
+      // the staged row scales: one 8-byte word (256 columns) per tile row
+      const int rl = threadIdx.x;
+      uint8_t* dst = a.row_scales + tile_elem / 32 + uint32_t(rl) * (Cu / 32);
+      if constexpr (CB == 6) store_sc1_8(dst, lds_rs[2 * rl], lds_rs[2 * rl + 1]);
+      else *reinterpret_cast<uint2*>(dst) = make_uint2(lds_rs[2 * rl], lds_rs[2 * rl + 1]);
     }
     if (lines6) {
       // the staged 6-bit row codes: 12 chunks of 16 bytes per tile row, through L2

@@ -17,7 +17,7 @@ struct CastArgs {
   int64_t rows, cols;     // per batch slice
   int64_t elements;       // batch * rows * cols
   uint32_t tiles_r, tiles_c;
-  uint32_t flags;         // kRowScaleDword / kColScaleDword / kStaggerStrips
+  uint32_t flags;         // kRowScaleDword / kColScaleDword / kStaggerStrips / kRowScaleQword
   uint32_t seed_lo, seed_hi;   // Philox key of stochastic rounding
 };
 
@@ -30,6 +30,10 @@ constexpr uint32_t kNvMarkedAmax = 4u;   // NVFP4 cast: global_scale holds marke
 // Tiled MX cast: rotate each XCD strip's walk over the tile rows (tile_coords).
 // Set by the host when the column plane's pitch is a multiple of 4 KiB.
 constexpr uint32_t kStaggerStrips = 8u;
+// Tiled MX cast with both copies and 1x32 blocks: every tile is 256 columns
+// wide (cols % 256 == 0) and the row-scale plane is 8-byte aligned, so a tile
+// row's 8 row-scale bytes can be stored as one 8-byte word.
+constexpr uint32_t kRowScaleQword = 16u;
 
 struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;

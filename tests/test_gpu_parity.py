@@ -160,6 +160,33 @@ def test_ragged_shapes(mx, fmt, dt):
             check(mx, x, fmt, mode, axis, f"ragged {(b, r, c, axis, mode)}")
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m3", "int8", "e2m1"])
+def test_row_scale_words(mx, fmt):
+    """Fused casts with cols % 256 == 0 store each tile row's 8 row-scale bytes
+    as one word after the barrier: batches, a ragged last tile row (160 and
+    4128 rows), sentinel-filled outputs, and a row-scale plane offset by 4 bytes
+    (not 8-byte aligned), which must take the per-wave stores instead."""
+    g = torch.Generator().manual_seed(31)
+    bits = {"e4m3": 8, "e2m3": 6, "int8": 8, "e2m1": 4}[fmt]
+    for b, r, c in [(2, 160, 512), (1, 4128, 256), (3, 64, 768)]:
+        x = (torch.randn((b, r, c), generator=g) *
+             torch.exp2(torch.randint(-10, 10, (b, r, c // 32), generator=g).float()).repeat_interleave(32, dim=2))
+        x = x.to(torch.bfloat16)
+        exp = oracle_quant(x, fmt, "floor", "both")
+        for shift in (0, 4):
+            rs = torch.full((b * r * (c // 32) + 8,), 0xA5, dtype=torch.uint8, device="cuda")
+            out = {"row_codes": torch.full((b, r, c * bits // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+                   "row_scales": rs[shift:shift + b * r * (c // 32)].view(b, r, c // 32),
+                   "col_codes": torch.full((b, c, r * bits // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+                   "col_scales": torch.full((b, c, r // 32), 0xA5, dtype=torch.uint8, device="cuda")}
+            got = mx.mx_quantize(x.cuda(), fmt, "floor", "both", out=out)
+            torch.cuda.synchronize()
+            got = {k: v.cpu().numpy() for k, v in got.items()}
+            assert_same(got, exp, f"row scale words {(b, r, c, fmt, shift)}")
+            guard = rs.cpu().numpy()
+            assert (guard[:shift] == 0xA5).all() and (guard[shift + b * r * (c // 32):] == 0xA5).all()
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
 def test_fp6_row_lines(mx, fmt, dt):
