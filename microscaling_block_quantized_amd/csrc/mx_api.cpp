@@ -227,6 +227,7 @@ int mx_quantize_nvfp4(const void* x, mx_dtype x_dtype, mx_shape s, mx_axis axis,
   a.flags = 0;
   if (want_row && s.cols % 64 == 0 && aligned(row_scales, 4)) a.flags |= mx::kRowScaleDword;
   if (want_col && s.rows % 64 == 0 && aligned(col_scales, 4)) a.flags |= mx::kColScaleDword;
+  if (want_row && want_col && s.cols % 256 == 0 && aligned(row_scales, 16)) a.flags |= mx::kNvRowScaleWords;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = x_dtype == MX_BF16;
   if (!global_given) {

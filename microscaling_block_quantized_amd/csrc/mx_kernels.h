@@ -34,6 +34,9 @@ constexpr uint32_t kStaggerStrips = 8u;
 // wide (cols % 256 == 0) and the row-scale plane is 8-byte aligned, so a tile
 // row's 8 row-scale bytes can be stored as one 8-byte word.
 constexpr uint32_t kRowScaleQword = 16u;
+// NVFP4 cast with both copies: cols % 256 == 0 and the row-scale plane 16-byte
+// aligned, so a tile row's 16 row-scale bytes can be stored as one 16-byte word.
+constexpr uint32_t kNvRowScaleWords = 32u;
 
 struct CastGrid {
   int64_t tiles_r, tiles_c, blocks;
@@ -63,7 +66,8 @@ struct NvArgs {
   float* global_scale;         // [batch]; with kNvMarkedAmax, raw marked maxima that the cast turns into g
   int64_t rows, cols;
   uint32_t tiles_r, tiles_c;
-  uint32_t flags;              // kRowScaleDword: cols % 64 == 0; kColScaleDword: rows % 64 == 0
+  uint32_t flags;              // kRowScaleDword: cols % 64 == 0; kColScaleDword: rows % 64 == 0;
+                               // kNvMarkedAmax; kNvRowScaleWords
 };
 
 // gs[b] = (largest finite |x| of slice b) as FP32 bits with the sign bit set

@@ -216,6 +216,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   // conflicts between the row groups of a wave.
   constexpr bool ROWLDS = ROWS && COLS;
   __shared__ __attribute__((aligned(16))) uint8_t lds_rows[ROWLDS ? kTileR * kTileC / 2 : 16];
+  // Row scales of full-width tiles (kNvRowScaleWords): a tile row's 16 scale
+  // bytes (4 dwords from 2 waves) are staged and leave as one 16-byte store
+  // after the barrier.
+  __shared__ __attribute__((aligned(16))) uint32_t lds_rs[ROWLDS ? kTileR * 4 : 4];
   auto rows_off = [](int r, int c) { return r * (kTileC / 2) + ((c / 2) ^ (((r >> 3) & 7) << 4)); };
 
   uint32_t bi, tr, tcol;
@@ -226,6 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   const int rows_in = int(min<int64_t>(R - r0, kTileR));
   const int cols_in = int(min<int64_t>(C - c0, kTileC));
   const uint32_t Cu = uint32_t(C);
+  const bool rs16 = ROWLDS && (a.flags & kNvRowScaleWords) != 0;
   // a marked value is the slice's raw amax: divide it here and publish g
   const uint32_t gbits = __float_as_uint(a.global_scale[bi]);
   float g = __uint_as_float(gbits);
@@ -338,7 +343,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         sb |= dpp<kDppRor4>(sb);
         sb |= dpp<kDppRor8>(sb);
       }
-      if (t % HALF == 0 && lrow + k < rows_in && dcol < cols_in) {
+      if (rs16) {
+        if (t % HALF == 0) lds_rs[(lrow + k) * 4 + dcol / 64] = sb;
+      } else if (t % HALF == 0 && lrow + k < rows_in && dcol < cols_in) {
         uint8_t* dst = sdst + int64_t(k) * C / 16;
         if (a.flags & kRowScaleDword) {
           *reinterpret_cast<uint32_t*>(dst) = sb;
@@ -421,6 +428,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
           }
         }
       }
+    }
+    if (rs16 && int(threadIdx.x) < rows_in) {
+      const int rl = threadIdx.x;
+      uint8_t* dst = a.row_scales + ((int64_t(bi) * R + r0 + rl) * C + c0) / 16;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(lds_rs + rl * 4);
     }
     if (int(threadIdx.x) < cols_in) {
       const int cl = threadIdx.x;

@@ -191,3 +191,28 @@ def test_given_global_scale_extremes(mx, gval):
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in out.items()}
     same(got, oracle(x, "both", gs.numpy()), f"given {gval}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_row_scale_words(mx, dt):
+    """With both copies, cols % 256 == 0 and a 16-byte-aligned row-scale plane,
+    a tile row's 16 row-scale bytes are stored as one word after the barrier:
+    batches, ragged tile rows, sentinel-filled outputs, and a plane offset by
+    4 bytes that must take the per-wave stores instead."""
+    g = torch.Generator().manual_seed(33)
+    for b, r, c in [(2, 160, 512), (1, 4128, 256), (3, 64, 768)]:
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-6, 6, (b, r, 1), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
+        exp = oracle(x, "both")
+        n = b * r * (c // 16)
+        for shift in (0, 4):
+            rs = torch.full((n + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+            out = {"row_codes": torch.full((b, r, c // 2), 0xA5, dtype=torch.uint8, device="cuda"),
+                   "row_scales": rs[shift:shift + n].view(b, r, c // 16),
+                   "col_codes": torch.full((b, c, r // 2), 0xA5, dtype=torch.uint8, device="cuda"),
+                   "col_scales": torch.full((b, c, r // 16), 0xA5, dtype=torch.uint8, device="cuda")}
+            got = mx.mx_quantize_nvfp4(x.cuda(), "both", out=out)
+            torch.cuda.synchronize()
+            same({k: v.cpu().numpy() for k, v in got.items()}, exp, f"nvfp4 row scale words {(b, r, c, dt, shift)}")
+            guard = rs.cpu().numpy()
+            assert (guard[:shift] == 0xA5).all() and (guard[shift + n:] == 0xA5).all()
