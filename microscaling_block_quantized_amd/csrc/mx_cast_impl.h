@@ -543,8 +543,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
     if (lines6) {
       // the staged 6-bit row codes: 12 chunks of 16 bytes per tile row, through L2
-      // (lines at the tile's edges are shared with the neighbouring tile); a
-      // ragged tile's last chunk may hold 8 valid bytes
+      // (lines at the tile's edges are shared with the neighbouring tile). With
+      // cols % 64 == 0 a ragged tile holds 48, 96 or 144 bytes per row, whole
+      // chunks; the 8-byte branch only guards a partial one.
       uint8_t* rct = reinterpret_cast<uint8_t*>(a.row_codes) + tile_elem * 6 / 8;
       const uint32_t rpitch = Cu * 6 / 8;
       const int bytes_in = cols_in * 6 / 8;
