@@ -235,6 +235,16 @@ int mx_quantize_fp4_fp8(const void* x, mx_dtype x_dtype, mx_shape s, mx_scale_mo
                         void* fp4_codes, uint8_t* fp4_scales, uint8_t* fp8, float* block_scale, uint8_t* fp8_t,
                         float* block_scale_t, uint8_t* spread, void* stream);
 
+/* Measurement helper, not an MX operation: copies `bytes` from src to dst with
+ * 16-byte non-temporal loads and stores, one chunk per thread. It moves the
+ * same kind of read and write traffic as a cast with no arithmetic, which makes
+ * it the bandwidth ceiling the casts are compared against. src and dst are
+ * caller-owned device memory, 16-byte aligned, not overlapping;
+ * bytes > 0 and bytes % 16 == 0. Enqueued on `stream`. Errors: MX_ERR_NULL,
+ * MX_ERR_SHAPE (size), MX_ERR_ALIGN, MX_ERR_ALIAS, MX_ERR_TOO_LARGE,
+ * MX_ERR_LAUNCH. */
+int mx_copy_nt(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Static text for an MX_* code; never NULL. */
 const char* mx_strerror(int err);
 

@@ -24,7 +24,7 @@ import os
 __all__ = [
     "MXError", "FMT", "CODE_BITS", "MODE", "AXIS", "DTYPE", "ROUNDING", "BLOCK", "MxQuantOpts", "lib_path", "load", "mx_version", "mx_strerror",
     "mx_plane_bytes", "mx_quantize", "mx_dequantize", "mx_quantize_nvfp4", "mx_dequantize_nvfp4",
-    "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "EXPORTS", "BoundQuantize", "BoundDequantize",
+    "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "mx_copy_nt", "EXPORTS", "BoundQuantize", "BoundDequantize",
     "BoundQuantizeNvfp4", "BoundRequant", "BoundQuantizeFp4Fp8",
 ]
 
@@ -36,8 +36,8 @@ ROUNDING = {"rne": 0, "sr": 1}
 BLOCK = {"1x32": 0, "32x32": 1}
 DTYPE = {"f32": 0, "bf16": 1}
 EXPORTS = ("mx_plane_bytes", "mx_quantize", "mx_quantize_ex", "mx_dequantize", "mx_dequantize_ex",
-           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "mx_strerror",
-           "mx_version")
+           "mx_quantize_nvfp4", "mx_dequantize_nvfp4", "mx_requant_fp4_fp8", "mx_quantize_fp4_fp8", "mx_copy_nt",
+           "mx_strerror", "mx_version")
 
 _LIB = None
 
@@ -95,6 +95,8 @@ def load() -> ctypes.CDLL:
     lib.mx_requant_fp4_fp8.argtypes = [vp, u8p, MxShape, i32, u8p, vp, u8p, vp, u8p, vp]
     lib.mx_quantize_fp4_fp8.restype = i32
     lib.mx_quantize_fp4_fp8.argtypes = [vp, i32, MxShape, i32, i32, vp, u8p, u8p, vp, u8p, vp, u8p, vp]
+    lib.mx_copy_nt.restype = i32
+    lib.mx_copy_nt.argtypes = [vp, vp, ctypes.c_int64, vp]
     _LIB = lib
     return lib
 
@@ -105,6 +107,22 @@ def mx_version() -> int:
 
 def mx_strerror(err: int) -> str:
     return load().mx_strerror(int(err)).decode()
+
+
+def mx_copy_nt(src, dst) -> None:
+    """Copy GPU tensor src into dst (same byte size, a multiple of 16) with the
+    library's plain non-temporal copy kernel: the bandwidth ceiling the casts
+    are measured against, not an MX operation."""
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("mx_copy_nt needs GPU tensors (libmx has no CPU path)")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("mx_copy_nt needs contiguous tensors of the same byte size")
+    import torch
+    with torch.cuda.device(src.device):
+        err = load().mx_copy_nt(_ptr(src), _ptr(dst), n, _stream_of(src))
+    if err:
+        raise MXError(err, "mx_copy_nt")
 
 
 def _shape3(shape) -> tuple:

@@ -55,7 +55,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10500; }
+int mx_version(void) { return 10600; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -159,6 +159,16 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
   if (sr) e = mx::launch_cast_sr(bf, int(fmt), int(mode), int(axis), b2d, a, nb, st);
   else if (b2d) e = mx::launch_cast_2d(bf, int(fmt), int(mode), int(axis), a, nb, st);
   else e = mx::launch_cast(bf, int(fmt), int(mode), int(axis), a, nb, st);
+  return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+int mx_copy_nt(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr) return MX_ERR_NULL;
+  if (bytes <= 0 || bytes % 16 != 0) return MX_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MX_ERR_ALIGN;
+  if (overlap(range_of(src, bytes), range_of(dst, bytes))) return MX_ERR_ALIAS;
+  if (mx::copy_blocks(bytes) > kMaxGrid) return MX_ERR_TOO_LARGE;
+  const hipError_t e = mx::launch_copy_nt(src, dst, bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 

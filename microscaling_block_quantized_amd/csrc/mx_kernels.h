@@ -100,6 +100,10 @@ enum RqSource : int { kFromMx = 0, kFromBf16 = 1, kFromF32 = 2 };
 // mode: the MXFP4 scale rule (kFloor / kRoundUp) when casting from x.
 hipError_t launch_requant(int src, int mode, int axis, const RqArgs& a, hipStream_t s);
 
+// Plain 16-byte non-temporal copy (mx_copy.hip); bytes % 16 == 0, 16-byte aligned.
+int64_t copy_blocks(int64_t bytes);
+hipError_t launch_copy_nt(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 // Dequantize n elements (n % 32 == 0) laid out with blocks along the flat order,
 // or, when cols > 0, with 32x32 blocks over rows of `cols` elements (scale
 // of element (r, c): scales[(r / 32) * (cols / 32) + c / 32], r counting

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10500
+    assert mxb.mx_version() == 10600
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -248,3 +248,19 @@ def test_quantize_fp4_fp8_argument_errors(lib):
     assert qq(c=C_ + 4) == E_ALIGN
     assert qq(c=X_ + 64) == E_ALIAS                              # MXFP4 codes over the weights
     assert qq(shape=(1, 1, 1 << 22), axis=1, ft=0, bt=0) == E_BIG
+
+
+def test_copy_argument_errors(lib):
+    """mx_copy_nt (the plain copy used as the bandwidth ceiling): every error
+    path returns before any HIP call."""
+    v = lambda p: ctypes.c_void_p(p)
+    cp = lambda src=X, dst=Y, n=4096: lib.mx_copy_nt(v(src), v(dst), n, None)
+    assert cp(src=0) == E_NULL
+    assert cp(dst=0) == E_NULL
+    assert cp(n=0) == E_SHAPE
+    assert cp(n=-16) == E_SHAPE
+    assert cp(n=4100) == E_SHAPE
+    assert cp(src=X + 8) == E_ALIGN
+    assert cp(dst=Y + 4) == E_ALIGN
+    assert cp(dst=X + 1024) == E_ALIAS
+    assert cp(src=Y + 2048) == E_ALIAS

@@ -100,3 +100,20 @@ def test_device_argument_errors(mx):
     with pytest.raises(mx.MXError) as e:
         mx.mx_quantize(x, "e4m3", "floor", "row", out={"row_codes": misaligned})
     assert e.value.code == -3
+
+
+def test_copy_nt(mx):
+    """The plain non-temporal copy: every byte copied, nothing written outside
+    the destination, on the caller's stream."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for nbytes in (16, 4096, 4096 * 257 + 48, 64 << 20):
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+        buf, dst = guarded(nbytes)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            mx.mx_copy_nt(src, dst)
+        s.synchronize()
+        assert torch.equal(dst, src), nbytes
+        host = buf.cpu().numpy()
+        assert (host[:GUARD] == CANARY).all() and (host[GUARD + nbytes:] == CANARY).all()
