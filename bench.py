@@ -197,6 +197,29 @@ SQ_KERNELS = {
     "act_e2m3": ("mx_cast_kernel<true, 3, 0, 3, 0, false>", ROWS * COLS),
     "grad_sr_e2m1": ("mx_cast_kernel<false, 2, 1, 2, 1, false>", 8192 * 8192),
 }
+# VALU issue peak of MI355X, non-packed: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_T_LANE_OPS = 256 * 4 * 16 * 2.4e9 / 1e12          # 39.32 T lane-ops/s
+# workloads whose main kernel is bound by VALU work and its latency, not HBM
+ALU_BOUND = ("grad_sr_e2m1",)
+SQ_PROFILE = os.path.join(ROOT, "profiles", "valu_lds_counters.md")
+
+
+def valu_ops_per_element(workload: str):
+    """VALU lane-ops per element of the workload's main kernel, from the committed
+    instruction-counter summary, or None."""
+    if not os.path.exists(SQ_PROFILE):
+        return None
+    with open(SQ_PROFILE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 5 and cells[0] == workload:
+                try:
+                    return float(cells[4])
+                except ValueError:
+                    return None
+    return None
+
+
 SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
                "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR")
 
@@ -679,6 +702,16 @@ def main() -> int:
                          "frac_of_ceiling": round(gbs / copy_gbs, 4),
                          "torch_device_copy": round(torch_copy_gbs, 2)},
     }
+    ops = valu_ops_per_element(args.workload) if args.workload in ALU_BOUND else None
+    if ops is not None:
+        # VALU-bound: the roofline is the VALU issue rate; the HBM view stays beside it
+        elems = SQ_KERNELS[args.workload][1]
+        tops = ops * elems / (ms * 1e-3) / 1e12
+        line["hbm_roofline"] = line["roofline"]
+        line["roofline"] = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_T_LANE_OPS, 2),
+                            "unit": "T VALU lane-ops/s", "frac": round(tops / VALU_PEAK_T_LANE_OPS, 4),
+                            "traffic": None, "valu_lane_ops_per_element": ops,
+                            "source": "profiles/valu_lds_counters.md (SQ_INSTS_VALU x 64 / elements)"}
     if not args.no_cpu_baseline and args.workload == "activations":
         import mx_inputs as I
         xa = I.activations(ROWS, COLS, seed=1, device=dev)
