@@ -377,7 +377,8 @@ def _cast_workload(gen, b, r, c, esize, fmt, mode, axis, desc, rounding="rne", b
     cfg = {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": fmt, "scale_mode": mode, "axis": axis}
     if rounding != "rne" or block != "1x32":
         cfg.update(rounding=rounding, block=block)
-    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "config": cfg}
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "config": cfg,
+            "dtype": "bf16" if esize == 2 else "f32"}
 
 
 def _nvfp4_workload():
@@ -400,7 +401,7 @@ def _nvfp4_workload():
         return mx.BoundQuantizeNvfp4(x, "both", out)
     desc = ("activations 16384x4096 bf16 -> NVFP4 (E2M1, 16-element UE4M3 blocks, FP32 global scale) row+col, "
             "global scale computed in the call")
-    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "dtype": "bf16",
             "config": {"workload": desc, "batch": b, "rows": r, "cols": c, "fmt": "nvfp4", "axis": "both",
                        "input_reads": 2}}
 
@@ -430,7 +431,7 @@ def _requant_workload():
     desc = ("weights 14336x4096 as MXFP4 (E2M1 1x32, floor) -> FP8 E4M3 with 128x128 power-of-two block scales, "
             "row copy + transposed copy + scale-spread check")
     # 16 sets: 500 MB of MXFP4 inputs, so none is still in the 256 MB memory-side cache when its turn comes
-    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "sets": 16,
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "sets": 16, "dtype": "u8",
             "config": {"workload": desc, "rows": r, "cols": c, "fmt": "e2m1->e4m3", "axis": "both"}}
 
 
@@ -458,7 +459,7 @@ def _qat_workload():
         return mx.BoundQuantizeFp4Fp8(x, "floor", "both", out)
     desc = ("FP32 master weights 14336x4096 -> MXFP4 (E2M1 1x32, floor) -> FP8 E4M3 with 128x128 power-of-two "
             "block scales in one pass: MXFP4 plane + row copy + transposed copy + spreads")
-    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}",
+    return {"bytes": nbytes, "make": make, "metric": f"GB/s (read+write), {desc}", "dtype": "f32",
             "config": {"workload": desc, "rows": r, "cols": c, "fmt": "f32->e2m1->e4m3", "axis": "both"}}
 
 
@@ -485,7 +486,7 @@ def _wide_range_pipeline():
             dr()
             dc()
         return step
-    return {"bytes": nbytes, "make": make, "sets": 1,
+    return {"bytes": nbytes, "make": make, "sets": 1, "dtype": "bf16",
             "metric": "GB/s (read+write), 64x4096x14336 BF16 MXFP8 E4M3 row+col quantize + both dequantizes",
             "config": {"workload": "wide-range batch 64x4096x14336 bf16: fused E4M3 quantize (floor), then "
                                    "row and column planes dequantized to bf16",
@@ -512,7 +513,7 @@ def _fp32_normal_round_trip():
             q()
             d()
         return step
-    return {"bytes": nbytes, "make": make,
+    return {"bytes": nbytes, "make": make, "dtype": "f32",
             "metric": "GB/s (read+write), 256x1024 FP32 MXFP8 E4M3 row quantize + dequantize",
             "config": {"workload": "fp32 N(0,1) 256x1024: row-wise E4M3 quantize (floor) + dequantize to fp32",
                        "rows": r, "cols": c, "fmt": "e4m3", "scale_mode": "floor", "axis": "row"}}
@@ -689,7 +690,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.get("dtype", "bf16"),
         "data": "synthetic",
         "config": dict(wl["config"], buffer_sets=args.sets, alg_bytes_per_step=alg_bytes),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
