@@ -327,6 +327,11 @@ static int rq_launch(int src, int mode, const void* x, const void* codes, const 
   a.tiles_r = uint32_t(tiles_r);
   a.tiles_c = uint32_t(tiles_c);
   a.total_tiles = uint32_t(blocks);
+  a.flags = 0;
+  // only with both copies: measured 2.2% faster there, but 2-3.5% slower for a
+  // single copy
+  if (src == mx::kFromMx && want_row && want_col && s.cols % 256 == 0 && aligned(scales, 4))
+    a.flags |= mx::kRqScaleWords;
   const hipError_t e = mx::launch_requant(src, mode, int(axis), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

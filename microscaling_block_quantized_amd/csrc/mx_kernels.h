@@ -95,7 +95,12 @@ struct RqArgs {
   int64_t rows, cols;
   uint32_t tiles_r, tiles_c;   // 128-row x 256-column tiles per slice
   uint32_t total_tiles;        // batch * tiles_r * tiles_c: one workgroup each
+  uint32_t flags;              // kRqScaleWords
 };
+// Requantization from an MXFP4 plane, with both copies, cols % 256 == 0
+// (every tile full width) and a 4-byte-aligned scale plane: each thread loads
+// one dword of its tile's scales (tile row t / 2, bytes 4 (t & 1) .. +3) into LDS.
+constexpr uint32_t kRqScaleWords = 1u;
 enum RqSource : int { kFromMx = 0, kFromBf16 = 1, kFromF32 = 2 };
 // mode: the MXFP4 scale rule (kFloor / kRoundUp) when casting from x.
 hipError_t launch_requant(int src, int mode, int axis, const RqArgs& a, hipStream_t s);

@@ -128,6 +128,8 @@ template <int SRC, int M, bool ROWS, bool COLS>
 __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
   __shared__ uint32_t part[kRqWaves][2];
   __shared__ __attribute__((aligned(16))) uint8_t lds_t[COLS ? kRqCols * kRqRows : 16];
+  // the tile's 128 x 8 scale bytes, loaded as one dword per thread (kRqScaleWords)
+  __shared__ __attribute__((aligned(4))) uint8_t lds_k[SRC == kFromMx ? kRqRows * 8 : 4];
 
   const uint32_t per_slice = a.tiles_r * a.tiles_c;
   const uint32_t bi = blockIdx.x / per_slice;
@@ -152,15 +154,39 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
     // tile origins (always inside the tensor); a lane outside it reads the origin instead
     const uint8_t* ct = a.codes + tile_row * (C / 2) + c0 / 2;
     const uint8_t* st = a.scales + tile_row * (C / 32) + c0 / 32;
+    if (a.flags & kRqScaleWords) {
 #pragma unroll
-    for (int i = 0; i < kRqRowsPerThread; ++i) {
-      const int row = kRqRowsPerThread * g + i;
-      const bool ok = col_ok && row < rows_in;
-      const u32x2 d = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x2*>(ct + (ok ? uint32_t(row) * (Cu / 2) + 8u * h : 0u)));
-      const uint32_t kk = st[ok ? uint32_t(row) * (Cu / 32) + sbk : 0u];
-      w[i] = ok ? make_uint2(d.x, d.y) : make_uint2(0u, 0u);
-      k[i] = ok ? kk : 0u;
+      for (int i = 0; i < kRqRowsPerThread; ++i) {
+        const int row = kRqRowsPerThread * g + i;
+        const bool ok = col_ok && row < rows_in;
+        const u32x2 d = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(ct + (ok ? uint32_t(row) * (Cu / 2) + 8u * h : 0u)));
+        w[i] = ok ? make_uint2(d.x, d.y) : make_uint2(0u, 0u);
+      }
+      // full-width tiles: thread t brings dword t & 1 of tile row t / 2's 8 scale
+      // bytes into LDS (one load instead of 8 byte loads per thread)
+      const int srow = t >> 1;
+      const uint32_t kw = srow < rows_in
+                              ? *reinterpret_cast<const uint32_t*>(st + uint32_t(srow) * (Cu / 32) + 4u * uint32_t(t & 1))
+                              : 0u;
+      reinterpret_cast<uint32_t*>(lds_k)[t] = kw;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kRqRowsPerThread; ++i) {
+        const int row = kRqRowsPerThread * g + i;
+        k[i] = (col_ok && row < rows_in) ? uint32_t(lds_k[row * 8 + sbk]) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRqRowsPerThread; ++i) {
+        const int row = kRqRowsPerThread * g + i;
+        const bool ok = col_ok && row < rows_in;
+        const u32x2 d = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(ct + (ok ? uint32_t(row) * (Cu / 2) + 8u * h : 0u)));
+        const uint32_t kk = st[ok ? uint32_t(row) * (Cu / 32) + sbk : 0u];
+        w[i] = ok ? make_uint2(d.x, d.y) : make_uint2(0u, 0u);
+        k[i] = ok ? kk : 0u;
+      }
     }
   } else {
     constexpr bool BF16 = SRC == kFromBf16;
