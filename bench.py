@@ -109,7 +109,7 @@ TRACE_KERNELS = {
                         [("mx_cast_kernel<true, 2, 0, 3, 0, true>", "mx_cast_kernel<bf16,E2M1,floor,row+col,32x32>",
                           _RQ_N * 2 + 2 * (_RQ_N // 2 + _RQ_N // 1024))]),
     "weights_fp4_in_fp8": ("MXFP4 -> FP8 128x128 requantization, row + transposed copy + spreads, 14336x4096",
-                           [("requant_kernel<true, true>", "requant_kernel<row+col>",
+                           [("requant_kernel<0, 0, true, true>", "requant_kernel<row+col>",
                              _RQ_N // 2 + _RQ_N // 32 + 2 * (_RQ_N + 4 * (_RQ_N // 16384)) + _RQ_N // 16384)]),
 }
 
@@ -149,7 +149,7 @@ COUNTER_KERNELS = {
                          _RQ_N * 2, 2 * (_RQ_N // 2 + _RQ_N // 1024))],
     "act_nvfp4": [("nv_amax_kernel<true>", "nv_amax_kernel<bf16>", _NV_N * 2, 0),
                   ("nv_cast_kernel<true, 3>", "nv_cast_kernel<bf16,row+col>", _NV_N * 2, 2 * (_NV_N // 2 + _NV_N // 16))],
-    "weights_fp4_in_fp8": [("requant_kernel<true, true>", "requant_kernel<row+col>", _RQ_N // 2 + _RQ_N // 32,
+    "weights_fp4_in_fp8": [("requant_kernel<0, 0, true, true>", "requant_kernel<row+col>", _RQ_N // 2 + _RQ_N // 32,
                             2 * (_RQ_N + 4 * (_RQ_N // 16384)) + _RQ_N // 16384)],
 }
 
