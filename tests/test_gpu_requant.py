@@ -66,6 +66,16 @@ def test_shapes_and_ragged_edges(mx, axis):
         check(mx, codes, scales, axis, f"{(b, r, c)}")
 
 
+def test_scale_words_batches_and_ragged_rows(mx):
+    """Both copies with cols % 256 == 0 load each tile's scales as one dword per
+    thread through LDS: batches, ragged last tile rows (272 and 64 rows) and
+    several tile columns, with NaN-scale sub-blocks."""
+    rng = np.random.default_rng(74)
+    for b, r, c in [(2, 272, 512), (3, 64, 768), (1, 400, 1024)]:
+        codes, scales = plane(rng, b, r, c, 100, 12, nan_frac=0.002)
+        check(mx, codes, scales, "both", f"{(b, r, c)}")
+
+
 def test_row_copy_accepts_any_row_count(mx):
     rng = np.random.default_rng(72)
     for r in (1, 37, 129, 255):
