@@ -264,3 +264,32 @@ def test_copy_argument_errors(lib):
     assert cp(dst=Y + 4) == E_ALIGN
     assert cp(dst=X + 1024) == E_ALIAS
     assert cp(src=Y + 2048) == E_ALIAS
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/libmx.h is a C header: a strict C99 program includes it, links
+    against libmx.so and makes host-side calls (sizes and error paths only)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_libmx.c"
+    src.write_text(
+        '#include "libmx.h"\n'
+        "int main(void) {\n"
+        "  mx_shape s = {1, 32, 64};\n"
+        "  size_t code = 0, scale = 0;\n"
+        "  if (mx_plane_bytes(MX_E2M1, s, &code, &scale) != MX_OK) return 1;\n"
+        "  if (code != 1024 || scale != 64) return 2;\n"
+        "  if (mx_quantize(0, MX_BF16, s, MX_E4M3, MX_SCALE_FLOOR, MX_AXIS_BOTH, 0, 0, 0, 0, 0) != MX_ERR_NULL) return 3;\n"
+        "  if (mx_copy_nt(0, 0, 16, 0) != MX_ERR_NULL) return 4;\n"
+        "  return mx_strerror(MX_ERR_ALIGN)[0] == 0;\n"
+        "}\n")
+    libdir = os.path.dirname(mxb.lib_path())
+    exe = tmp_path / "use_libmx"
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-L", libdir, "-lmx", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(exe)]).returncode == 0
