@@ -9,38 +9,51 @@ magnitude divided by 6 * 448; a 16-element block takes 16 * 4 + 8 = 72 bits
 (4.5 bits per element); decoding multiplies by the FP8 block scale and the FP32
 global scale. §7 warns that the block scale is unsigned.
 
-The pages leave the arithmetic order open. Because floating point decides the
-integer codes here, the readings below fix every step in FP32 (IEEE, round to
-nearest-even), the precision the format itself names; this module performs
-those steps with numpy float32 operations, one at a time:
+The pages state what each scale is, not the arithmetic that produces the
+codes (§7 counts the order of applying the two scales among the points an
+implementation still has to get right). The plainest reading, taken here, is
+the exact one:
+every code is the round-to-nearest-even of an exact real quotient, and only the
+two values the format itself stores in FP32 are rounded to FP32.
 
   * A = largest |x| over the tensor's finite elements (one tensor = one batch
-    slice); g = fp32(A / 2688) is the global (decode) scale.
-  * Block scale: t = fp32(fp32(amax_b / 6) / g), encoded as E4M3 with
-    round-to-nearest-even, saturating at 448, sign bit 0 (UE4M3).
-  * Elements: q = fp32(x * r_b) with r_b = fp32(1 / fp32(s_b * g)) and s_b the
-    decoded block scale (the §4 table applies NVFP4's scales by multiplication),
-    encoded as E2M1 with round-to-nearest-even and saturation at 6.
-  * A block whose scale code is 0 (all-zero blocks, and blocks too small for
-    UE4M3 relative to g), whose r_b is not finite (fp32(s_b * g) is 0 or below
-    2^-128), and every block of a tensor with g == 0, store codes 0.
-  * A block holding NaN or +-Inf gets the UE4M3 NaN code 0x7F and element codes 0;
-    A ignores non-finite elements.
-  * Decoding: y = fp32(fp32(e2m1 * ue4m3) * g) (the first product is exact);
-    BF16 output is that FP32 value rounded to nearest-even. A NaN block scale
-    decodes to NaN.
+    slice); g = the FP32 value nearest to A / 2688 (the stored global scale).
+  * Block scale code: the UE4M3 value nearest to the exact quotient
+    amax_b / (6 * g), ties to the even code, saturating at 448, sign bit 0.
+  * Element code: the E2M1 value nearest to the exact quotient x / (s_b * g),
+    s_b the decoded block scale, ties to the even code, saturating at 6; the
+    sign bit is the sign of x (including -0).
+  * Decoding: y = FP32 of the exact product e2m1 * s_b * g (one rounding;
+    e2m1 * s_b is exact in FP32, so this equals fp32(fp32(e2m1 * s_b) * g),
+    the FP8-then-FP32 multiply of the §4 table). BF16 output is that FP32
+    value rounded to nearest-even. A NaN block scale decodes to NaN.
+
+Readings where the pages give nothing (the quotient has no value):
+  * a block whose scale code is 0 (an all-zero block, or a block whose amax is
+    below half of UE4M3's smallest step relative to 6 * g) stores codes 0;
+  * a g that is not a finite positive number (an all-zero tensor gives g = 0;
+    a caller may pass any g) makes every block store scale 0 and codes 0;
+  * a block holding NaN or +-Inf gets the UE4M3 NaN code 0x7F and element
+    codes 0; A ignores non-finite elements.
   * Layout: codes as MXFP4 (two per byte, element 2k in the low nibble), block
     scales [B][R][C/16] (column copy [B][C][R/16]), global scales [B] FP32;
     the column copy is the same cast of X^T with the same global scale.
+
+Exactness. Both roundings compare a numerator with (grid midpoint) x (divisor),
+never dividing. Each such product is exact in float64: a UE4M3 midpoint has at
+most 5 significant bits, 6 has 2 and an FP32 g 24 (31 bits in all); an E2M1
+midpoint has at most 3 and s_b at most 4 (31 bits with g). The numerators are
+FP32 or BF16 values, exact in float64, so every comparison is exact.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .mx_oracle import E2M1, E4M3, ROW, COL, encode_elements, pack_e2m1, unpack_e2m1, value_table, widen, \
-    bf16_bits
+from .mx_oracle import E2M1, E4M3, ROW, COL, positive_grid, pack_e2m1, unpack_e2m1, value_table, widen, \
+    f32_bits, bf16_bits
 
-__all__ = ["NV_BLOCK", "nvfp4_global_scale", "nvfp4_quantize", "nvfp4_dequantize", "ue4m3_encode"]
+__all__ = ["NV_BLOCK", "nvfp4_global_scale", "nvfp4_quantize", "nvfp4_dequantize", "ue4m3_encode",
+           "nearest_code_of_quotient"]
 
 NV_BLOCK = 16          # [Q] §3 table: 16 elements per block
 E2M1_MAX = 6.0         # [Q] §3: 6 is E2M1's largest value
@@ -52,17 +65,46 @@ def _f32(v):
     return np.asarray(v, dtype=np.float32)
 
 
+def nearest_code_of_quotient(num: np.ndarray, den: np.ndarray, fmt) -> np.ndarray:
+    """Magnitude code of the value of fmt nearest to num / den, exactly.
+
+    num >= 0 and den > 0 are float64 arrays (broadcast together) such that
+    every product (midpoint of two neighbouring grid values) * den is exact in
+    float64. The quotient is compared with the midpoints between neighbouring
+    values of fmt's non-negative grid; at a midpoint the neighbour with the
+    even code wins ([Q] §2: round to nearest, ties to even); beyond the
+    largest value the largest value is taken ([Q] §4: clip).
+    """
+    codes, vals = positive_grid(fmt)
+    mids = (vals[:-1] + vals[1:]) / 2                   # exact: a midpoint needs one bit more than its neighbours
+    num, den = np.broadcast_arrays(np.asarray(num, np.float64), np.asarray(den, np.float64))
+    num, den = num.reshape(-1), den.reshape(-1)
+    out = np.empty(num.shape, np.int64)
+    step = max(1, (1 << 22) // len(mids))               # bounds the threshold matrix to ~32 MB
+    for i0 in range(0, num.size, step):
+        n = num[i0:i0 + step, None]
+        thr = mids[None, :] * den[i0:i0 + step, None]   # exact products (see the module note)
+        idx = (n > thr).sum(axis=1)                     # midpoints strictly below num / den
+        # a quotient exactly at midpoint idx goes up when the upper neighbour's code is even
+        at = np.take_along_axis(n == thr, np.minimum(idx, len(mids) - 1)[:, None], axis=1)[:, 0] & (idx < len(mids))
+        up = at & (codes[np.minimum(idx + 1, len(codes) - 1)] % 2 == 0)
+        out[i0:i0 + step] = codes[idx + up.astype(np.int64)]
+    return out
+
+
 def nvfp4_global_scale(x64: np.ndarray) -> np.ndarray:
-    """FP32 global scale per batch slice: fp32(A / (6 * 448)), A over finite elements."""
+    """FP32 global scale per batch slice: the FP32 value nearest to A / (6 * 448),
+    A over finite elements (IEEE float32 division rounds the exact quotient once)."""
     b = x64.shape[0]
     a = np.abs(np.where(np.isfinite(x64), x64, 0.0)).reshape(b, -1).max(axis=1)
-    return _f32(a) / np.float32(E2M1_MAX * UE4M3_MAX)          # FP32 division, RNE
+    return _f32(a) / np.float32(E2M1_MAX * UE4M3_MAX)
 
 
-def ue4m3_encode(t: np.ndarray) -> np.ndarray:
-    """Non-negative FP32 values -> E4M3 codes (sign bit 0), RNE, saturating at 448."""
-    t = np.asarray(t, dtype=np.float64)
-    return encode_elements(np.minimum(t, UE4M3_MAX), E4M3)
+def ue4m3_encode(amax: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """UE4M3 code nearest to amax / (6 * g) (amax >= 0 float64, g > 0 FP32), RNE, saturating at 448."""
+    amax = np.asarray(amax, np.float64)
+    den = np.float64(E2M1_MAX) * np.asarray(g, np.float64)      # exact: 2 + 24 bits
+    return nearest_code_of_quotient(amax, den, E4M3).reshape(np.broadcast(amax, den).shape).astype(np.uint8)
 
 
 def _quant_plane(x64: np.ndarray, g: np.ndarray):
@@ -71,22 +113,18 @@ def _quant_plane(x64: np.ndarray, g: np.ndarray):
     finite = np.isfinite(blocks)
     special = ~finite.all(axis=3)
     clean = np.where(finite, blocks, 0.0)
-    amax = _f32(np.abs(clean).max(axis=3))                      # exact: inputs are FP32 or BF16
-    gg = g.reshape(b, 1, 1)
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        t = (amax / np.float32(E2M1_MAX)) / gg                  # two FP32 divisions
-    t = np.where(gg == 0, np.float32(0), t)
-    scode = ue4m3_encode(t)
-    sval = _f32(value_table(E4M3)[scode])
-    den = sval * gg                                             # FP32 product
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        rb = np.float32(1) / den                                # FP32 division
-        q = _f32(clean) * rb[..., None]                         # FP32 product
-    zero = ((scode == 0) | ~np.isfinite(rb))[..., None]       # r_b overflows for a tiny s_b * g
-    q = np.where(zero, np.float32(0), q)
-    codes = encode_elements(q.astype(np.float64), E2M1)
+    amax = np.abs(clean).max(axis=3)                            # exact: inputs are FP32 or BF16
+    g64 = np.asarray(g, np.float64).reshape(b, 1, 1)
+    g_ok = np.isfinite(g64) & (g64 > 0)
+    scode = ue4m3_encode(amax, np.where(g_ok, g64, 1.0) * np.ones_like(amax))
+    scode = np.where(g_ok, scode, 0).astype(np.uint8)
+    sval = value_table(E4M3)[scode.astype(np.int64)]
+    den = (sval * np.where(g_ok, g64, 1.0))[..., None]          # s_b * g: exact in float64 (28 bits)
+    zero = (scode == 0)[..., None] | special[..., None]
+    mag = nearest_code_of_quotient(np.abs(clean), np.where(zero, 1.0, den) * np.ones_like(clean), E2M1)
+    mag = mag.reshape(clean.shape)
+    codes = mag | (np.signbit(clean).astype(np.int64) << 3)
     codes = np.where(zero, 0, codes).astype(np.uint8)
-    codes = np.where(special[..., None], 0, codes).astype(np.uint8)
     scode = np.where(special, UE4M3_NAN, scode).astype(np.uint8)
     return pack_e2m1(codes.reshape(b, r, c)), scode
 
@@ -110,20 +148,23 @@ def nvfp4_quantize(x: np.ndarray, in_dtype: str, axis: int, global_scale: np.nda
 
 
 def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, global_scale: np.ndarray, out_dtype: str):
-    """codes [B][N][M/2], scales [B][N][M/16], global_scale [B] -> FP32 / BF16 bits."""
+    """codes [B][N][M/2], scales [B][N][M/16], global_scale [B] -> FP32 / BF16 bits.
+
+    y = e2m1 * s_b * g, formed exactly in float64 (at most 6 + 24 significant
+    bits) and rounded once to FP32; BF16 output rounds that FP32 value."""
     c = unpack_e2m1(codes)
     b = c.shape[0]
-    ev = _f32(value_table(E2M1)[c])
-    sv = _f32(value_table(E4M3)[np.asarray(scales, dtype=np.int64)])
+    ev = value_table(E2M1)[c]
+    sv = value_table(E4M3)[np.asarray(scales, dtype=np.int64)]
     sv = np.repeat(sv, NV_BLOCK, axis=-1)
-    g = _f32(global_scale).reshape((b,) + (1,) * (c.ndim - 1))
-    y = (ev * sv) * g                                           # FP32: exact product, then one rounding
+    g = np.asarray(global_scale, np.float32).astype(np.float64).reshape((b,) + (1,) * (c.ndim - 1))
     nan = np.repeat(np.asarray(scales) == UE4M3_NAN, NV_BLOCK, axis=-1)
-    y = np.where(nan, np.float32(np.nan), y)
-    bits = y.view(np.uint32).copy()
-    bits[np.isnan(y)] = 0x7FC00000
+    with np.errstate(invalid="ignore"):
+        y = np.where(nan, np.nan, ev * sv * g)
+    bits32 = f32_bits(y)
     if out_dtype == "f32":
-        return bits
+        return bits32
     if out_dtype == "bf16":
-        return bf16_bits(y.astype(np.float64))
+        y32 = bits32.view(np.float32).astype(np.float64)
+        return bf16_bits(y32)
     raise ValueError(f"unknown output dtype {out_dtype!r}")

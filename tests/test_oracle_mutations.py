@@ -303,14 +303,20 @@ def planted_nv(name, fn):
         setattr(O, name, old)
 
 
+NV_PINS = [(PN.test_global_scale_is_amax_over_6_times_448, ()),
+           (PN.test_block_scale_brute_force_at_every_ue4m3_value_and_midpoint, ()),
+           (PN.test_element_codes_brute_force_under_every_block_scale, (np.float32(1.0) / np.float32(3.0),)),
+           (PN.test_midpoint_ties_go_to_even_codes, ()), (PN.test_block_holding_the_tensor_max_decodes_exactly, ()),
+           (PN.test_random_blocks_brute_force, ())]
+
+
 def test_pins_catch_nvfp4_global_scale_without_the_6():
     def g448(x64):
         b = x64.shape[0]
         a = np.abs(np.where(np.isfinite(x64), x64, 0.0)).reshape(b, -1).max(axis=1)
         return a.astype(np.float32) / np.float32(448.0)
     with planted_nv("nvfp4_global_scale", g448):
-        assert any_pin_fails([(PN.test_global_scale_is_amax_over_6_times_448, ()),
-                              (PN.test_block_holding_the_tensor_max_decodes_exactly, ())])
+        assert any_pin_fails(NV_PINS)
 
 
 def test_pins_catch_nvfp4_elements_scaled_without_global():
@@ -319,8 +325,54 @@ def test_pins_catch_nvfp4_elements_scaled_without_global():
     def no_global(x64, g):
         return orig(x64, np.ones_like(g))
     with planted_nv("_quant_plane", no_global):
-        assert any_pin_fails([(PN.test_block_holding_the_tensor_max_decodes_exactly, ()),
-                              (PN.test_scale_steps_match_torch_float32, ())])
+        assert any_pin_fails(NV_PINS)
+
+
+def test_pins_catch_nvfp4_fp32_reciprocal_chain():
+    """Every step in FP32: block code of fp32(fp32(amax / 6) / g), elements
+    fp32(x * fp32(1 / fp32(s * g))), each then rounded to the grid."""
+    def chain(x64, g):
+        b, r, c = x64.shape
+        blocks = x64.reshape(b, r, c // 16, 16)
+        special = ~np.isfinite(blocks).all(axis=3)
+        clean = np.where(np.isfinite(blocks), blocks, 0.0)
+        amax = np.abs(clean).max(axis=3).astype(np.float32)
+        gg = np.asarray(g, np.float32).reshape(b, 1, 1)
+        with np.errstate(all="ignore"):
+            t = (amax / np.float32(6)) / gg
+            scode = M.encode_elements(np.minimum(t.astype(np.float64), 448.0), M.E4M3)
+            rb = np.float32(1) / (M.value_table(M.E4M3)[scode].astype(np.float32) * gg)
+            q = clean.astype(np.float32) * rb[..., None]
+        zero = (scode == 0)[..., None] | special[..., None] | ~np.isfinite(rb)[..., None]
+        codes = np.where(zero, 0, M.encode_elements(np.where(zero, 0.0, q.astype(np.float64)), M.E2M1))
+        scode = np.where(special, 0x7F, scode).astype(np.uint8)
+        return M.pack_e2m1(codes.astype(np.uint8).reshape(b, r, c)), scode
+    with planted_nv("_quant_plane", chain):
+        assert any_pin_fails(NV_PINS)
+
+
+def test_pins_catch_nvfp4_block_scale_rounded_twice():
+    def twice(amax, g):
+        with np.errstate(all="ignore"):
+            t = (np.asarray(amax, np.float32) / np.float32(6)) / np.asarray(g, np.float32)
+        return M.encode_elements(np.minimum(t.astype(np.float64), 448.0), M.E4M3).astype(np.uint8)
+    with planted_nv("ue4m3_encode", twice):
+        assert any_pin_fails(NV_PINS)
+
+
+def test_pins_catch_nvfp4_ties_away_from_zero():
+    orig = NV.nearest_code_of_quotient
+
+    def away(num, den, fmt):
+        codes = orig(num, den, fmt)
+        cs, vals = M.positive_grid(fmt)
+        mids = (vals[:-1] + vals[1:]) / 2
+        n, d = (a.reshape(-1) for a in np.broadcast_arrays(np.asarray(num, np.float64), np.asarray(den, np.float64)))
+        for k, m in enumerate(mids):
+            codes = np.where(n == m * d, cs[k + 1], codes)     # every tie goes up
+        return codes
+    with planted_nv("nearest_code_of_quotient", away):
+        assert any_pin_fails(NV_PINS)
 
 
 import oracle.nested as NS  # noqa: E402
