@@ -3,18 +3,16 @@
 // "MXFP4 と NVFP4 は何が違うのか調べてみた" §3, the §4 table and §7: E2M1 elements
 // (the same as MXFP4's) in blocks of 16, each block with an unsigned E4M3
 // (UE4M3, largest value 448) scale, and one FP32 global scale per tensor equal
-// to the tensor's largest magnitude over 6 * 448. Every scale step is one FP32
-// operation with round-to-nearest-even (IEEE-correct division), in this order:
-//   g = A / 2688                          (A: largest finite |x| of the batch slice)
-//   t = (amax_b / 6) / g    -> UE4M3      (RNE, saturating at 448)
-//   r_b = 1 / (s_b * g)                   (per block; the §4 table applies NVFP4's
-//   q = x * r_b             -> E2M1        scales by multiplication; RNE, saturating at 6)
-//   y = (e2m1 * s_b) * g                  (dequantization; the first product is exact)
-// A block whose scale code is 0, or whose r_b is not finite, or every block
-// when g == 0, stores codes 0; a block holding NaN or Inf stores the UE4M3 NaN
-// code 0x7F and codes 0. Codes are packed as MXFP4's (element 2k in the low nibble);
-// block scales are [B][R][C/16] and, for the column copy (the same cast of
-// X^T), [B][C][R/16].
+// to the tensor's largest magnitude over 6 * 448. The codes are the exact ones:
+//   g   = fp32(A / 2688)                (A: largest finite |x| of the batch slice)
+//   s_b = UE4M3 nearest to amax_b / (6 g)   (exact quotient, RNE, saturating at 448)
+//   q   = E2M1 nearest to x / (s_b g)       (exact quotient, RNE, saturating at 6)
+//   y   = fp32(fp32(e2m1 * s_b) * g)    (dequantization; the first product is exact)
+// A block whose scale code is 0, and every block when g is not a finite
+// positive number, stores codes 0; a block holding NaN or Inf stores the UE4M3
+// NaN code 0x7F and codes 0. Codes are packed as MXFP4's (element 2k in the low
+// nibble); block scales are [B][R][C/16] and, for the column copy (the same
+// cast of X^T), [B][C][R/16].
 //
 // g takes two launches and the cast: zero the caller's [B] FP32 array, then
 // fold every workgroup's amax into it with one atomic max, as FP32 bits with
@@ -24,28 +22,49 @@
 // The cast reuses the MX tiled kernel's layout (128 x 256 tiles, 8 waves,
 // LDS-staged column codes).
 //
-// The cast never divides per element and rarely per block:
-//  * r_b depends only on the block's scale code, so each workgroup divides once
-//    per code (256 entries in LDS, shared by the tile).
-//  * The block code is first estimated as fp32(amax_b * k), k = fp32(fp32(1/6) *
-//    fp32(1/g)). Every rounding in the exact and the estimated chain is relative
-//    error at most 2^-24 while amax_b >= 2^-120 and 2^-125 <= g <= 2^100, so the
-//    estimate is within 6 FP32 ulps of the exact t. E4M3 rounding is monotone:
-//    when t - 16 ulps and t + 16 ulps round to the same code, that is the code
-//    of the exact t. Otherwise, or outside those ranges, the block takes the
-//    two IEEE divisions.
+// The cast never divides per element and rarely per block, and decides every
+// code exactly:
+//  * Block code: estimated as fp32(amax_b * k), k = fp32(fp32(1/6) * fp32(1/g)),
+//    within 4 FP32 ulps of the exact amax_b / (6 g) while amax_b >= 2^-120 and
+//    2^-125 <= g <= 2^100. E4M3 rounding is monotone: when t - 16 ulps and
+//    t + 16 ulps round to the same code, that is the code of the exact quotient.
+//    Any other block compares amax_b with (midpoint x 6 g) in FP64, which is
+//    exact (at most 5 + 2 + 24 significant bits).
+//  * Elements: r_b = fp32(1 / fp32(s_b g)) depends only on the block code, so
+//    each workgroup divides once per code (256 entries in LDS). q' = fp32(x r_b)
+//    is within 3 FP32 ulps of the exact quotient Q = x / (s_b g), which is not
+//    enough near an E2M1 midpoint, and with BF16 inputs Q lands next to short
+//    binary values often (g = fp32(A / 2688) has a periodic significand). So
+//    every element is decided exactly, without a branch, on magnitudes: m = the
+//    E4M3 value nearest to min(|q'|, 8) (one paired conversion there and back).
+//    All E2M1 values and midpoints are E4M3 values, so when m is not a midpoint
+//    |q'| and m round alike. sigma = fma(-(m s_b), g, |x|) has the exact sign
+//    of |Q| - m (m s_b has at most 8 significant bits, and for
+//    2^-90 <= g <= 2^100 a nonzero |x| - m s_b g is at least 2^-149 in
+//    magnitude, so the one rounding keeps it nonzero). m moved by up to 2^-10
+//    towards |Q| (not at all when sigma is 0, an exact tie), with the sign of x,
+//    then takes the hardware E2M1 rounding, which is the exact code: the move
+//    is more than an FP32 ulp of m when m is a midpoint and less than m's
+//    distance to any other rounding boundary. With g outside that range every element compares
+//    |x| with (midpoint x s_b g) in FP64 instead (exact: 3 + 4 + 24 bits).
 #include "mx_cast_impl.h"
 
 namespace mx {
 
 namespace {
 
-constexpr float kE2m1Max = 6.0f;
 constexpr float kNvGlobalDiv = 6.0f * 448.0f;      // 2688
 constexpr float kRcp6 = 0x1.555556p-3f;            // fp32(1/6)
 constexpr uint32_t kNvWindow = 16;                 // ulps each side of the estimate
 constexpr uint32_t kNvTcap = 0x49800000u;          // 2^20: every t above 464 saturates alike
 constexpr uint32_t kNvAmin = 0x03800000u;          // 2^-120: amax/6 stays a normal FP32
+// Element decision: sigma * (r_b * 2^24) moves m by at least 2^-12 when sigma
+// is not 0 (a nonzero sigma is at least 2^-34 |x|, and m >= 0.25 at a midpoint),
+// and the move is clamped to 2^-10.
+constexpr float kNvNudgeGain = 0x1p24f;
+constexpr float kNvNudge = 0x1p-10f;
+// global scales for which the element decision above is exact
+constexpr float kNvGmin = 0x1p-90f, kNvGmax = 0x1p100f;
 
 // ---------------- global scale ----------------
 
@@ -137,14 +156,34 @@ __device__ __forceinline__ NvScale nv_scale(float g) {
   return s;
 }
 
-// The defining computation: E4M3 of fp32(fp32(amax / 6) / g), RNE, overflow
-// (0x7F) stepped down to 448. amag: FP32 bits of the block's largest magnitude
+// UE4M3 value of code c (0 .. 0x7E) in FP64: subnormals m * 2^-9, normals (8 + m) * 2^(e - 10).
+__device__ __forceinline__ double ue4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return __builtin_ldexp(double(e == 0 ? m : 8u + m), e == 0 ? -9 : int(e) - 10);
+}
+
+// The defining computation: the UE4M3 code nearest to amax / (6 g), ties to the
+// even code, saturating at 0x7E (448). Midpoint i lies between codes i and
+// i + 1, and the code is the number of midpoints the quotient passes (strictly
+// above, or on one whose upper neighbour is even), found by binary search over
+// exact FP64 comparisons of amax with (midpoint x 6 g) (at most 5 + 2 + 24
+// significant bits). amag: FP32 bits of the block's largest magnitude
 // (>= 0x7F800000: NaN or Inf present).
 __device__ __forceinline__ uint32_t nv_code_exact(uint32_t amag, float g) {
   if (amag >= 0x7F800000u) return 0x7Fu;
-  if (g == 0.0f) return 0u;
-  const float t = (__uint_as_float(amag) / kE2m1Max) / g;
-  return fix_overflow<kE4M3>(cvt2_f32<kE4M3, false>(0u, t, 0.0f, scale_operand(127u))) & 0xFFu;
+  if (!(g > 0.0f && g < __builtin_inff())) return 0u;
+  const double num = double(__uint_as_float(amag));
+  const double den = 6.0 * double(g);                  // exact: 2 + 24 bits
+  uint32_t lo = 0, hi = 0x7Eu;
+#pragma unroll 1
+  while (lo < hi) {
+    const uint32_t i = (lo + hi) >> 1;
+    const double t = 0.5 * (ue4m3_value(i) + ue4m3_value(i + 1)) * den;
+    const bool up = num > t || (num == t && (i & 1u));
+    lo = up ? i + 1 : lo;
+    hi = up ? hi : i;
+  }
+  return lo;
 }
 
 // The same code through the estimate, falling back to nv_code_exact.
@@ -162,15 +201,15 @@ __device__ __forceinline__ uint32_t nv_code(uint32_t amag, const NvScale& s) {
   return c;
 }
 
-// LDS table of 1 / fp32(s_c * g) for every scale byte c; NaN marks the codes
-// whose blocks store codes 0 (c == 0, or the reciprocal is not finite).
+// LDS table of 1 / fp32(s_c * g) for every scale byte c (g in [2^-90, 2^100]);
+// NaN marks the codes whose blocks store codes 0 (c == 0 and the NaN code 0x7F).
 constexpr int kNvTab = 256;
 __device__ __forceinline__ void nv_fill_table(float* tab, float g) {
   const int c = threadIdx.x;
   if (c < kNvTab) {
     const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uint32_t(c), scale_operand(127u), false)[0];
     const float r = 1.0f / (s * g);
-    tab[c] = (c == 0 || !(__builtin_fabsf(r) < __builtin_inff())) ? __builtin_nanf("") : r;
+    tab[c] = (c == 0 || c == 0x7F) ? __builtin_nanf("") : r;
   }
 }
 
@@ -182,12 +221,85 @@ __device__ __forceinline__ NvBlock nv_block(uint32_t amag, const NvScale& s, con
   return b;
 }
 
-// Four FP32 values times the block's reciprocal -> four E2M1 codes in the low 16 bits.
-__device__ __forceinline__ uint32_t nv_encode4(float f0, float f1, float f2, float f3, const NvBlock& b) {
+// E2M1 code of x / (s_b g), decided exactly: binary search for the number of
+// midpoints |x| passes, comparing with (midpoint x s_b g) in FP64 (exact: at
+// most 3 + 4 + 24 bits); on a midpoint, up when the upper neighbour's code is
+// even (midpoints 1, 3 and 5). The midpoints are 2^-2 * (1, 3, 5, 7, 10, 14, 20),
+// packed as 5-bit fields of kNvMid4.
+constexpr uint64_t kNvMid4 = 1ull | 3ull << 5 | 5ull << 10 | 7ull << 15 | 10ull << 20 | 14ull << 25 | 20ull << 30;
+__device__ __forceinline__ uint32_t nv_code1_exact(float f, double d) {
+  const double a = __builtin_fabs(double(f));
+  uint32_t lo = 0, hi = 7;
+#pragma unroll 1
+  while (lo < hi) {
+    const uint32_t i = (lo + hi) >> 1;
+    const double t = double(uint32_t(kNvMid4 >> (5 * i)) & 31u) * 0.25 * d;
+    const bool up = a > t || (a == t && (i & 1u));
+    lo = up ? i + 1 : lo;
+    hi = up ? hi : i;
+  }
+  return lo | ((__float_as_uint(f) >> 28) & 8u);
+}
+
+// One element's exactly rounded quotient stand-in (see the header), worked on
+// magnitudes: m, the E4M3 value nearest to min(|q'|, 8), moved by at most 2^-10
+// towards |x| / (s_b g), kept at least 2^-100 (no subnormal reaches the
+// conversion), and given the sign of x (so that -0 and tiny negative x code as -0).
+__device__ __forceinline__ float nv_nudged(float f, float m, float ms, float g, float gain) {
+  const float sigma = __builtin_fmaf(-ms, g, __builtin_fabsf(f));   // exact sign of |x| - m s_b g
+  const float mag = __builtin_fmaxf(m + __builtin_amdgcn_fmed3f(sigma * gain, -kNvNudge, kNvNudge), 0x1p-100f);
+  return __builtin_copysignf(mag, f);
+}
+
+// Four FP32 values -> four E2M1 codes in the low 16 bits, each the exact
+// rounding of x / (s_b g) (see the header).
+__device__ __forceinline__ uint32_t nv_encode4(float f0, float f1, float f2, float f3, const NvBlock& b,
+                                               float g) {
   const float one = scale_operand(127u);
-  uint32_t w = cvt2_fp4_f32<0>(0u, f0 * b.rcp, f1 * b.rcp, one);
-  w = cvt2_fp4_f32<1>(w, f2 * b.rcp, f3 * b.rcp, one);
-  return b.zero ? 0u : (w & 0xFFFFu);
+  {
+    const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.code, one, false)[0];
+    const float gain = b.rcp * kNvNudgeGain;
+    const float q0 = __builtin_fminf(__builtin_fabsf(f0) * b.rcp, 8.0f);
+    const float q1 = __builtin_fminf(__builtin_fabsf(f1) * b.rcp, 8.0f);
+    const float q2 = __builtin_fminf(__builtin_fabsf(f2) * b.rcp, 8.0f);
+    const float q3 = __builtin_fminf(__builtin_fabsf(f3) * b.rcp, 8.0f);
+    uint32_t e = cvt2_f32<kE4M3, false>(0u, q0, q1, one);       // nearest E4M3 values (no overflow at 8)
+    e = cvt2_f32<kE4M3, true>(e, q2, q3, one);
+    const float2v m01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, false);
+    const float2v m23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, true);
+    uint32_t w = cvt2_fp4_f32<0>(0u, nv_nudged(f0, m01.x, m01.x * s, g, gain),
+                                 nv_nudged(f1, m01.y, m01.y * s, g, gain), one);
+    w = cvt2_fp4_f32<1>(w, nv_nudged(f2, m23.x, m23.x * s, g, gain), nv_nudged(f3, m23.y, m23.y * s, g, gain), one);
+    return b.zero ? 0u : (w & 0xFFFFu);
+  }
+}
+
+// One 16-element block decided entirely in FP64 (g outside [2^-90, 2^100], or
+// not a finite positive number): 16 elements at stride `step` elements from p,
+// the 8 code bytes to `codes` (8-byte aligned) and the scale byte to `scale`.
+template <bool BF16>
+__device__ __forceinline__ void nv_block_exact(const uint8_t* p, int64_t step, float g, uint8_t* codes,
+                                               uint8_t* scale) {
+  float f[16];
+  uint32_t amag = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (BF16) {
+      f[i] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(p + i * step * 2)) << 16);
+    } else {
+      f[i] = *reinterpret_cast<const float*>(p + i * step * 4);
+    }
+    amag = max(amag, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  }
+  const uint32_t code = nv_code_exact(amag, g);
+  const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code, scale_operand(127u), false)[0];
+  const double d = double(s) * double(g);                       // exact: 4 + 24 bits
+  const bool zero = code == 0 || code == 0x7F;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= (zero ? 0u : nv_code1_exact(f[i], d)) << (4 * (i & 7));
+  *reinterpret_cast<uint2*>(codes) = make_uint2(w[0], w[1]);
+  *scale = uint8_t(code);
 }
 
 // ---------------- cast ----------------
@@ -239,6 +351,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     if (threadIdx.x == 0) a.global_scale[bi] = g;
   }
 
+  const int64_t tile_elem = (int64_t(bi) * R + r0) * C + c0;
+  const uint8_t* xt = reinterpret_cast<const uint8_t*>(a.x) + tile_elem * ES;
+  if (!(g >= kNvGmin && g <= kNvGmax)) {
+    // g outside [2^-90, 2^100] (or 0, negative, Inf, NaN): the whole slice is
+    // decided in FP64, one 16-element block per thread at a time
+    const int rb_row = cols_in / 16, rb_col = rows_in / 16;
+    if constexpr (ROWS) {
+#pragma unroll 1
+      for (int i = threadIdx.x; i < rows_in * rb_row; i += kThreads) {
+        const int r = i / rb_row, cb = i - r * rb_row;
+        const int64_t e = (int64_t(bi) * R + r0 + r) * C + c0 + 16 * cb;
+        nv_block_exact<BF16>(xt + (int64_t(r) * C + 16 * cb) * ES, 1, g,
+                             reinterpret_cast<uint8_t*>(a.row_codes) + e / 2, a.row_scales + e / 16);
+      }
+    }
+    if constexpr (COLS) {
+#pragma unroll 1
+      for (int i = threadIdx.x; i < cols_in * rb_col; i += kThreads) {
+        const int c = i / rb_col, rb = i - c * rb_col;
+        const int64_t e = (int64_t(bi) * C + c0 + c) * R + r0 + 16 * rb;
+        nv_block_exact<BF16>(xt + (int64_t(16 * rb) * C + c) * ES, C, g,
+                             reinterpret_cast<uint8_t*>(a.col_codes) + e / 2, a.col_scales + e / 16);
+      }
+    }
+    return;
+  }
+
   const int wid = threadIdx.x >> 6;
   const int wr = wid % kWaveRows, wc = wid / kWaveRows;
   const int lane = threadIdx.x & 63;
@@ -247,8 +386,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   const int lrow = 32 * wr + RPT * q;
   const bool col_ok = lcol < cols_in;
 
-  const int64_t tile_elem = (int64_t(bi) * R + r0) * C + c0;
-  const uint8_t* xt = reinterpret_cast<const uint8_t*>(a.x) + tile_elem * ES;
   const uint32_t xoff = (uint32_t(lrow) * Cu + uint32_t(lcol)) * ES;
   uint4 v[RPT];
 #pragma unroll
@@ -323,12 +460,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const bool ok = col_ok && lrow + k < rows_in;
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu / 2;
       if constexpr (BF16) {
-        const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk) |
-                           (nv_encode4(elem(k, 4), elem(k, 5), elem(k, 6), elem(k, 7), blk) << 16);
+        const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk, g) |
+                           (nv_encode4(elem(k, 4), elem(k, 5), elem(k, 6), elem(k, 7), blk, g) << 16);
         if constexpr (ROWLDS) *reinterpret_cast<uint32_t*>(lds_rows + rows_off(lrow + k, lcol)) = w;
         else if (ok) store_nt4(dst, w);
       } else {
-        const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk);
+        const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk, g);
         if constexpr (ROWLDS) *reinterpret_cast<uint16_t*>(lds_rows + rows_off(lrow + k, lcol)) = uint16_t(w);
         else if (ok) store_nt2(dst, w);
       }
@@ -366,14 +503,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int cl = lcol + j;
       const int off = cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
       if constexpr (BF16) {
-        const uint32_t w = nv_encode4(elem(0, j), elem(1, j), elem(2, j), elem(3, j), cb[j]) |
-                           (nv_encode4(elem(4, j), elem(5, j), elem(6, j), elem(7, j), cb[j]) << 16);
+        const uint32_t w = nv_encode4(elem(0, j), elem(1, j), elem(2, j), elem(3, j), cb[j], g) |
+                           (nv_encode4(elem(4, j), elem(5, j), elem(6, j), elem(7, j), cb[j], g) << 16);
         *reinterpret_cast<uint32_t*>(lds_codes + off) = w;               // 8 rows in 4 bytes
       } else {
         uint32_t w[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          w[g4] = nv_encode4(elem(4 * g4, j), elem(4 * g4 + 1, j), elem(4 * g4 + 2, j), elem(4 * g4 + 3, j), cb[j]);
+          w[g4] = nv_encode4(elem(4 * g4, j), elem(4 * g4 + 1, j), elem(4 * g4 + 2, j), elem(4 * g4 + 3, j), cb[j], g);
         *reinterpret_cast<uint2*>(lds_codes + off) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
       }
     }
@@ -451,8 +588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 
 template <bool BF16, int AX>
 hipError_t launch_nv_cast(const NvArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((nv_cast_kernel<BF16, AX>), dim3(nblocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(nv_cast_kernel<BF16, AX>, dim3(nblocks), dim3(kThreads), s, a);
 }
 
 template <bool BF16>
@@ -531,19 +667,16 @@ hipError_t launch_nvfp4_global(bool in_bf16, const void* x, int64_t batch, int64
                                hipStream_t s) {
   uint32_t* gb = reinterpret_cast<uint32_t*>(gs);
   const uint32_t small = uint32_t((batch + 255) / 256);
-  hipLaunchKernelGGL(nv_zero_kernel, dim3(small), dim3(256), 0, s, gb, batch);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(nv_zero_kernel, dim3(small), dim3(256), s, gb, batch);
   if (e != hipSuccess) return e;
   const int64_t chunks = slice_elems * (in_bf16 ? 2 : 4) / 16;
   const int64_t per_block = int64_t(kAmaxThreads) * kAmaxUnroll;
   const int64_t want = (chunks + per_block - 1) / per_block;
   const int64_t cap = batch >= kAmaxBlocks ? 1 : kAmaxBlocks / batch;
   const dim3 grid(uint32_t(want < cap ? want : cap), uint32_t(batch));
-  if (in_bf16)
-    hipLaunchKernelGGL(nv_amax_kernel<true>, grid, dim3(kAmaxThreads), 0, s, static_cast<const uint8_t*>(x), gb, chunks);
-  else
-    hipLaunchKernelGGL(nv_amax_kernel<false>, grid, dim3(kAmaxThreads), 0, s, static_cast<const uint8_t*>(x), gb, chunks);
-  return hipGetLastError();
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  return in_bf16 ? launch_kernel(nv_amax_kernel<true>, grid, dim3(kAmaxThreads), s, xb, gb, chunks)
+                 : launch_kernel(nv_amax_kernel<false>, grid, dim3(kAmaxThreads), s, xb, gb, chunks);
 }
 
 hipError_t launch_nvfp4_cast(bool in_bf16, int axis, const NvArgs& a, uint32_t nblocks, hipStream_t s) {
@@ -553,13 +686,10 @@ hipError_t launch_nvfp4_cast(bool in_bf16, int axis, const NvArgs& a, uint32_t n
 hipError_t launch_nvfp4_dequant(bool out_bf16, const uint8_t* codes, const uint8_t* scales, const float* gs,
                                 void* y, int64_t nblocks, int64_t blocks_per_slice, hipStream_t s) {
   const uint32_t grid = uint32_t((nblocks + kDqThreads - 1) / kDqThreads);
-  if (out_bf16)
-    hipLaunchKernelGGL(nv_dequant_kernel<true>, dim3(grid), dim3(kDqThreads), 0, s, codes, scales, gs, y, nblocks,
-                       blocks_per_slice);
-  else
-    hipLaunchKernelGGL(nv_dequant_kernel<false>, dim3(grid), dim3(kDqThreads), 0, s, codes, scales, gs, y, nblocks,
-                       blocks_per_slice);
-  return hipGetLastError();
+  return out_bf16 ? launch_kernel(nv_dequant_kernel<true>, dim3(grid), dim3(kDqThreads), s, codes, scales, gs, y,
+                                  nblocks, blocks_per_slice)
+                  : launch_kernel(nv_dequant_kernel<false>, dim3(grid), dim3(kDqThreads), s, codes, scales, gs, y,
+                                  nblocks, blocks_per_slice);
 }
 
 }  // namespace mx

@@ -216,3 +216,72 @@ def test_row_scale_words(mx, dt):
             same({k: v.cpu().numpy() for k, v in got.items()}, exp, f"nvfp4 row scale words {(b, r, c, dt, shift)}")
             guard = rs.cpu().numpy()
             assert (guard[:shift] == 0xA5).all() and (guard[shift + n:] == 0xA5).all()
+
+
+def _e2m1_midpoint_blocks(g, seed):
+    """FP32 blocks, for every UE4M3 block code s: a block max of fp32(6 s g)
+    and elements within 0, 1, 2, 5 and 40 FP32 ulps of every E2M1 value and
+    every midpoint between them, times s g, with random signs."""
+    rng = np.random.default_rng(seed)
+    vals = O.value_table(O.E4M3)[1:0x7F]
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    offs = np.array([0, 1, -1, 2, -2, 5, -5, 40, -40], np.int32)
+    blocks = []
+    for s in vals:
+        top = np.float32(6.0 * s * np.float64(g))
+        if not np.isfinite(top) or top == 0:
+            continue
+        el = (np.repeat(pts, len(offs)) * s * np.float64(g)).astype(np.float32)
+        el = (el.view(np.int32) + np.tile(offs, len(pts))).view(np.float32)
+        el = el[np.isfinite(el) & (el > 0) & (el <= top)]
+        el = el * np.where(rng.random(el.size) < 0.5, -1, 1).astype(np.float32)
+        pad = (-el.size) % 15
+        el = np.concatenate([el, np.zeros(pad, np.float32)]).reshape(-1, 15)
+        blocks.append(np.concatenate([np.full((el.shape[0], 1), top, np.float32), el], axis=1))
+    b = np.concatenate(blocks)
+    b = np.concatenate([b, np.zeros(((-len(b)) % 16, 16), np.float32)])
+    return torch.from_numpy(b.reshape(-1, 256))
+
+
+@pytest.mark.parametrize("gval", [1.0, 1.0 / 3.0, 0.0123, 2.0 ** -10, 2.0 ** -140, 3 * 2.0 ** -147])
+def test_element_codes_near_e2m1_midpoints(mx, gval):
+    """Elements next to every E2M1 rounding boundary under every block code:
+    the hardware rounding of x * r_b must give way to the exact comparison
+    wherever the two can differ (also where s_b * g is not a normal FP32)."""
+    gs = np.array([gval], np.float32)
+    x = _e2m1_midpoint_blocks(gs[0], seed=70)
+    x = torch.cat([x, torch.zeros(((-x.shape[0]) % 16, 256), dtype=x.dtype)])     # rows % 16 for the column copy
+    for xx, axis in ((x, "row"), (x.T.contiguous(), "both")):
+        out = mx.mx_quantize_nvfp4(xx.cuda(), axis, global_scale=torch.from_numpy(gs).cuda())
+        torch.cuda.synchronize()
+        same({k: v.cpu().numpy() for k, v in out.items()}, oracle(xx, axis, gs), f"e2m1 mid {gval} {axis}")
+    xb = x.to(torch.bfloat16)
+    check(mx, xb, "both", f"e2m1 mid bf16 {gval}")
+
+
+def test_midpoint_ties_with_computed_global_scale(mx):
+    """A = 2688 gives g = 1 and a block max of 18 the block scale 3: 0.75,
+    2.25, 7.5 and 15 sit exactly on E2M1 midpoints and go to the even codes."""
+    x = torch.zeros((32, 256), dtype=torch.float32)
+    x[0, 0] = 2688.0
+    x[1, :7] = torch.tensor([18.0, 0.75, -0.75, 2.25, 7.5, 15.0, 4.5])
+    for dt in (torch.float32, torch.bfloat16):
+        check(mx, x.to(dt), "both", f"ties {dt}")
+    out = mx.mx_quantize_nvfp4(x.cuda(), "row")
+    torch.cuda.synchronize()
+    assert out["row_scales"][1, 0].item() == 0x44
+    assert out["row_codes"][1, :4].cpu().tolist() == [0x07, 0x28, 0x64, 0x03]
+
+
+@pytest.mark.parametrize("gval", [-1.0, float("inf"), float("nan")])
+def test_unusable_given_global_scale(mx, gval):
+    """A given g that is not a finite positive number: scale 0 and codes 0 for
+    every finite block, 0x7F for blocks holding NaN or Inf."""
+    x = I.gradients(64, 96, seed=71)
+    gs = torch.tensor([gval], dtype=torch.float32)
+    out = mx.mx_quantize_nvfp4(x.cuda(), "both", global_scale=gs.cuda())
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    exp = oracle(x, "both", gs.numpy())
+    assert (exp["row_codes"] == 0).all() and (exp["row_scales"] != 0x7F).sum() == (exp["row_scales"] == 0).sum()
+    same(got, exp, f"unusable g {gval}")
