@@ -75,7 +75,7 @@ typedef struct {
 
 /* Rounding of the elements (same article: §2 requires round-to-nearest-even for
  * the FP4 conversion; §4's 4-bit pretraining recipe rounds gradients
- * stochastically, and §11 lists stochastic rounding among the P3109 modes).
+ * stochastically, and §8 lists stochastic rounding among the P3109 modes).
  * MX_ROUND_STOCHASTIC: a scaled value s with |s| < max goes to the grid value
  *   above |s| when the fraction f of |s| between its two neighbouring grid
  *   values exceeds u / 2^16, else to the one below; |s| >= max saturates; the
@@ -109,14 +109,20 @@ typedef struct {
 #define MX_ERR_ALIAS (-5)       /* input and an output overlap, or two outputs do */
 #define MX_ERR_TOO_LARGE (-6)   /* beyond one launch: cols >= 2^22, rows >= 2^23 with
                                    column planes, or more than 2^31-1 tiles */
-#define MX_ERR_LAUNCH (-7)      /* the kernel launch failed (hipGetLastError) */
+#define MX_ERR_LAUNCH (-7)      /* a kernel launch failed (the status hipLaunchKernel returned for it;
+                                   an error left by an unrelated earlier call is not read or cleared) */
 
-/* Bytes of ONE code plane and ONE scale plane for a tensor of shape s quantized
- * to fmt (both axes have the same sizes): code = batch*rows*cols*bits/8 (bits
- * 8, 6 or 4),
- * scale = batch*rows*cols/32. Shape rules are those of mx_quantize with
- * MX_AXIS_BOTH. Pure host arithmetic; no HIP call. */
-int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_bytes);
+/* Bytes of the code planes and of the scale planes that mx_quantize writes for
+ * a tensor of shape s, format fmt and the planes selected by axis (1x32
+ * blocks): each plane holds batch*rows*cols*bits/8 code bytes (bits 8, 6 or 4)
+ * and batch*rows*cols/32 scale bytes, and *code_bytes / *scale_bytes receive
+ * the totals over the selected planes (twice one plane for MX_AXIS_BOTH).
+ * Per element and plane that is bits + 8/32: 4.25 bits for MXFP4 and 8.25 for
+ * MXFP8 (same article, §2 family table; 6.25 for MXFP6, 8.25 for MXINT8).
+ * Shape rules: extents >= 1; cols % 32 == 0 with MX_AXIS_ROW; rows % 32 == 0
+ * with MX_AXIS_COL. Errors: MX_ERR_ENUM, MX_ERR_NULL, MX_ERR_SHAPE. Pure host
+ * arithmetic; no HIP call. */
+int mx_plane_bytes(mx_fmt fmt, mx_shape s, mx_axis axis, size_t* code_bytes, size_t* scale_bytes);
 
 /* Quantize x ([batch][rows][cols], x_dtype) into the planes selected by axis.
  *   row_codes  [batch][rows][cols] bytes, E2M1: [batch][rows][cols/2] with
@@ -127,9 +133,12 @@ int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_byt
  *              E2M3/E3M2: [batch][cols][3*rows/4]
  *   col_scales [batch][cols][rows/32]
  * Pointers of an axis not in `axis` must be NULL; the others must be non-NULL.
- * Shape: batch, rows, cols >= 1; cols % 32 == 0 always (16-byte vector rows);
- * rows % 32 == 0 when MX_AXIS_COL is set. x, row_codes and col_codes must be
- * 16-byte aligned. Inputs and outputs must not overlap. */
+ * Shape: batch, rows, cols >= 1; cols % 32 == 0 when MX_AXIS_ROW is set (the
+ * row blocks); rows % 32 == 0 when MX_AXIS_COL is set (the column blocks).
+ * A column-only cast blocks no run along cols, which then needs only rows of
+ * whole 16-byte vectors: cols % 8 == 0 (BF16) or cols % 4 == 0 (FP32).
+ * x, row_codes and col_codes must be 16-byte aligned. Inputs and outputs must
+ * not overlap. */
 int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
                 mx_axis axis, void* row_codes, uint8_t* row_scales, void* col_codes,
                 uint8_t* col_scales, void* stream);
@@ -147,8 +156,8 @@ int mx_dequantize(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_shape
 
 /* mx_quantize with options; opts == NULL means nearest-even and 1x32 blocks,
  * which is exactly mx_quantize. With MX_BLOCK_32X32 the scale planes hold
- * batch*rows*cols/1024 bytes each (layout above) and rows % 32 == 0 also for
- * MX_AXIS_ROW; the code planes are as for mx_quantize. Errors as mx_quantize,
+ * batch*rows*cols/1024 bytes each (layout above) and rows % 32 == 0 and
+ * cols % 32 == 0 for every axis; the code planes are as for mx_quantize. Errors as mx_quantize,
  * plus MX_ERR_ENUM for an unknown rounding or block. The result depends only on
  * the inputs, the options and the seed (not on the launch or the device). */
 int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
@@ -166,12 +175,13 @@ int mx_dequantize_ex(const void* codes, const uint8_t* scales, mx_fmt fmt, mx_sh
  * blocks of 16, each with an unsigned E4M3 (UE4M3, at most 448, sign bit 0)
  * block scale, and one FP32 global scale per tensor (per batch slice) equal
  * to the slice's largest finite magnitude A over 6 * 448; 4.5 bits per
- * element. Every step is one FP32 operation with round-to-nearest-even, in
- * this order: g = A / 2688; t = (amax_b / 6) / g -> UE4M3 (saturating at
- * 448); r_b = 1 / (s_b * g); q = x * r_b -> E2M1 (saturating at 6). A block
- * whose scale code is 0 or whose r_b is not finite, and every block when
- * g == 0, stores codes 0; a block holding NaN or Inf stores scale 0x7F (UE4M3
- * NaN) and codes 0.
+ * element. The codes are exact roundings of exact quotients:
+ * g = fp32(A / 2688); the block code is the UE4M3 value nearest to
+ * amax_b / (6 g) (ties to the even code, saturating at 448); each element
+ * code is the E2M1 value nearest to x / (s_b g) (ties to even, saturating at
+ * 6, sign of x). A block whose scale code is 0, and every block when g is
+ * not a finite positive number, stores codes 0; a block holding NaN or Inf
+ * stores scale 0x7F (UE4M3 NaN) and codes 0.
  *   global_scale  [batch] FP32, device memory: written (global_given == 0)
  *                 or read (global_given == 1, e.g. a scale kept from an
  *                 earlier step). When written, it holds intermediate values
@@ -224,7 +234,7 @@ int mx_requant_fp4_fp8(const void* codes, const uint8_t* scales, mx_shape s, mx_
 
 /* The quantization-aware step of the same section in one pass: master weights
  * x (BF16 or FP32, [batch][rows][cols]) are cast to MXFP4 exactly as
- * mx_quantize does with fmt = MX_FMT_E2M1, scale rule scale_mode and
+ * mx_quantize does with fmt = MX_E2M1, scale rule scale_mode and
  * MX_AXIS_ROW, and that MXFP4 plane is re-expressed as FP8 exactly as
  * mx_requant_fp4_fp8 does; the result equals the two calls in sequence.
  *   fp4_codes / fp4_scales  the MXFP4 plane ([batch][rows][cols/2], 8-byte

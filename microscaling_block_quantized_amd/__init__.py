@@ -10,11 +10,14 @@ The functions mirror the C ABI in ``include/libmx.h``:
                                             is not the default)
     mx_dequantize(codes, scales, fmt, shape, out_dtype, block)
     mx_quantize_nvfp4(x, axis, global_scale) / mx_dequantize_nvfp4(...)
-    mx_plane_bytes(fmt, shape)           -> (code bytes, scale bytes) of one plane
+    mx_plane_bytes(fmt, shape, axis)     -> (code bytes, scale bytes) of the planes of `axis`
     mx_strerror(err), mx_version()
 
 There is no CPU path: inputs must be GPU tensors, and a missing ``libmx.so``
-raises at the first call.
+raises at the first call. Before any call, every tensor is checked against
+the sizes the shape and format imply (dtype, contiguity, byte count, device):
+the C ABI trusts the caller's buffer sizes, so a short buffer would otherwise
+be written past its end.
 """
 from __future__ import annotations
 
@@ -76,7 +79,7 @@ def load() -> ctypes.CDLL:
     lib.mx_strerror.restype = ctypes.c_char_p
     lib.mx_strerror.argtypes = [i32]
     lib.mx_plane_bytes.restype = i32
-    lib.mx_plane_bytes.argtypes = [i32, MxShape, ctypes.POINTER(ctypes.c_size_t),
+    lib.mx_plane_bytes.argtypes = [i32, MxShape, i32, ctypes.POINTER(ctypes.c_size_t),
                                    ctypes.POINTER(ctypes.c_size_t)]
     lib.mx_quantize.restype = i32
     lib.mx_quantize.argtypes = [vp, i32, MxShape, i32, i32, i32, vp, u8p, vp, u8p, vp]
@@ -134,13 +137,72 @@ def _shape3(shape) -> tuple:
     return shape
 
 
-def mx_plane_bytes(fmt: str, shape) -> tuple:
+def mx_plane_bytes(fmt: str, shape, axis: str = "row") -> tuple:
+    """(code bytes, scale bytes) summed over the planes of `axis` (1x32 blocks)."""
     b, r, c = _shape3(shape)
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
-    err = load().mx_plane_bytes(FMT[fmt], MxShape(b, r, c), ctypes.byref(cb), ctypes.byref(sb))
+    err = load().mx_plane_bytes(FMT[fmt], MxShape(b, r, c), AXIS[axis], ctypes.byref(cb), ctypes.byref(sb))
     if err:
         raise MXError(err, "mx_plane_bytes")
     return cb.value, sb.value
+
+
+def _check(t, name: str, nbytes: int, dtype, dev) -> None:
+    """Raise ValueError unless t is a contiguous tensor of `dtype` on `dev`
+    holding exactly `nbytes` bytes."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    got = t.numel() * t.element_size()
+    if got != nbytes:
+        raise ValueError(f"{name} holds {got} bytes; this shape and format need {nbytes}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the input on {dev}")
+
+
+def _need_gpu(t, where: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{where} needs GPU tensors (libmx has no CPU path)")
+
+
+def _input(x, where: str):
+    """The input tensor's dtype code after the checks every cast makes."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"{where}: the input must be a bfloat16 or float32 tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{where}: the input must be contiguous")
+    return DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"]
+
+
+def _mx_plane_shapes(b, r, c, fmt: str, block: str) -> dict:
+    """Shapes of the four MX planes of a [b][r][c] tensor. For every shape the
+    C ABI accepts they hold exactly the bytes it writes; for any other shape
+    the C ABI rejects the call before touching a buffer."""
+    bits = CODE_BITS[fmt]
+    two = block == "32x32"
+    return {"row_codes": (b, r, c * bits // 8),
+            "row_scales": (b, max(r // 32, 1), c // 32) if two else (b, r, c // 32),
+            "col_codes": (b, c, r * bits // 8),
+            "col_scales": (b, c // 32, max(r // 32, 1)) if two else (b, c, max(r // 32, 1))}
+
+
+def _numel(shape) -> int:
+    n = 1
+    for v in shape:
+        n *= v
+    return n
+
+
+def _check_mx_planes(planes: dict, b, r, c, fmt: str, block: str, dev) -> None:
+    import torch
+    for k, shp in _mx_plane_shapes(b, r, c, fmt, block).items():
+        if k in planes:
+            _check(planes[k], k, _numel(shp), torch.uint8, dev)
 
 
 def _stream_of(t):
@@ -171,16 +233,10 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
     [B][C/32][R/32]) go through mx_quantize_ex.
     """
     import torch
-    if not x.is_cuda:
-        raise ValueError("mx_quantize needs a GPU tensor (libmx has no CPU path)")
-    if x.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError(f"unsupported input dtype {x.dtype}")
-    if not x.is_contiguous():
-        raise ValueError("input must be contiguous")
+    xdt = _input(x, "mx_quantize")
     b, r, c = _shape3(x.shape)
     squeeze = x.dim() == 2
     ax = AXIS[axis]
-    bits = CODE_BITS[fmt]
     out = out or {}
     dev = x.device
 
@@ -189,16 +245,13 @@ def mx_quantize(x, fmt: str = "e4m3", mode: str = "floor", axis: str = "both", o
         return t if t is not None else torch.empty(shp, dtype=torch.uint8, device=dev)
 
     opts = _opts(rounding, seed, block)
-    b2 = block == "32x32"
+    shapes = _mx_plane_shapes(b, r, c, fmt, block)
     planes = {}
-    if ax & 1:
-        planes["row_codes"] = plane("row_codes", (b, r, c * bits // 8))
-        planes["row_scales"] = plane("row_scales", (b, max(r // 32, 1), c // 32) if b2 else (b, r, c // 32))
-    if ax & 2:
-        planes["col_codes"] = plane("col_codes", (b, c, r * bits // 8))
-        planes["col_scales"] = plane("col_scales", (b, c // 32, max(r // 32, 1)) if b2 else (b, c, max(r // 32, 1)))
-    args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
-            MODE[mode], ax)
+    for k in (("row_codes", "row_scales") if ax & 1 else ()) + (("col_codes", "col_scales") if ax & 2 else ()):
+        planes[k] = plane(k, shapes[k])
+    _check_mx_planes(planes, b, r, c, fmt, block, dev)
+    _need_gpu(x, "mx_quantize")
+    args = (_ptr(x), xdt, MxShape(b, r, c), FMT[fmt], MODE[mode], ax)
     outs = (_ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")), _ptr(planes.get("col_codes")),
             _ptr(planes.get("col_scales")), _stream_of(x))
     with torch.cuda.device(dev):
@@ -218,15 +271,15 @@ def mx_dequantize(codes, scales, fmt: str, shape, out_dtype: str = "f32", out=No
     (blocks of 32 along its last axis, or 32x32 tiles with block "32x32").
     Returns a float32 or bfloat16 GPU tensor."""
     import torch
-    if not codes.is_cuda or not scales.is_cuda:
-        raise ValueError("mx_dequantize needs GPU tensors (libmx has no CPU path)")
-    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-        raise TypeError("codes and scales must be uint8")
-    if not codes.is_contiguous() or not scales.is_contiguous():
-        raise ValueError("codes and scales must be contiguous")
     b, r, c = _shape3(shape)
-    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=codes.device)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
+    dev = codes.device
+    shp = _mx_plane_shapes(b, r, c, fmt, block)
+    _check(codes, "codes", _numel(shp["row_codes"]), torch.uint8, dev)
+    _check(scales, "scales", _numel(shp["row_scales"]), torch.uint8, dev)
+    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=dev)
+    _check(y, "out", b * r * c * (2 if out_dtype == "bf16" else 4), tdt, dev)
+    _need_gpu(codes, "mx_dequantize")
     with torch.cuda.device(codes.device):
         if block == "1x32":
             err = load().mx_dequantize(_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c), DTYPE[out_dtype],
@@ -246,10 +299,15 @@ class BoundQuantize:
 
     def __init__(self, x, fmt: str, mode: str, axis: str, out: dict, rounding: str = "rne", seed: int = 0,
                  block: str = "1x32"):
-        import torch
         b, r, c = _shape3(x.shape)
-        head = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), FMT[fmt],
-                MODE[mode], AXIS[axis])
+        xdt = _input(x, "BoundQuantize")
+        ax = AXIS[axis]
+        names = (("row_codes", "row_scales") if ax & 1 else ()) + (("col_codes", "col_scales") if ax & 2 else ())
+        if set(k for k, v in out.items() if v is not None) != set(names):
+            raise ValueError(f"BoundQuantize: out must hold exactly {names}")
+        _check_mx_planes(out, b, r, c, fmt, block, x.device)
+        _need_gpu(x, "BoundQuantize")
+        head = (_ptr(x), xdt, MxShape(b, r, c), FMT[fmt], MODE[mode], ax)
         tail = (_ptr(out.get("row_codes")), _ptr(out.get("row_scales")), _ptr(out.get("col_codes")),
                 _ptr(out.get("col_scales")), _stream_of(x))
         self._opts = _opts(rounding, seed, block)
@@ -273,6 +331,14 @@ class BoundDequantize:
     def __init__(self, codes, scales, fmt: str, shape, y):
         import torch
         b, r, c = _shape3(shape)
+        dev = codes.device
+        shp = _mx_plane_shapes(b, r, c, fmt, "1x32")
+        _check(codes, "codes", _numel(shp["row_codes"]), torch.uint8, dev)
+        _check(scales, "scales", _numel(shp["row_scales"]), torch.uint8, dev)
+        if y.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("BoundDequantize: y must be bfloat16 or float32")
+        _check(y, "y", b * r * c * y.element_size(), y.dtype, dev)
+        _need_gpu(codes, "BoundDequantize")
         self._fn = load().mx_dequantize
         self._args = (_ptr(codes), _ptr(scales), FMT[fmt], MxShape(b, r, c),
                       DTYPE["bf16" if y.dtype == torch.bfloat16 else "f32"], _ptr(y), _stream_of(codes))
@@ -305,6 +371,15 @@ def _nv_planes(x, axis: str, out: dict | None):
     return planes
 
 
+def _check_nv_planes(planes: dict, b, r, c, dev) -> None:
+    import torch
+    _check(planes["global_scale"], "global_scale", 4 * b, torch.float32, dev)
+    for k, nb in (("row_codes", b * r * (c // 2)), ("row_scales", b * r * (c // 16)),
+                  ("col_codes", b * c * (r // 2)), ("col_scales", b * c * max(r // 16, 1))):
+        if k in planes:
+            _check(planes[k], k, nb, torch.uint8, dev)
+
+
 def mx_quantize_nvfp4(x, axis: str = "both", global_scale=None, out: dict | None = None):
     """NVFP4 cast of a GPU tensor [R][C] or [B][R][C] (bfloat16 or float32).
 
@@ -315,19 +390,18 @@ def mx_quantize_nvfp4(x, axis: str = "both", global_scale=None, out: dict | None
     tensor's own amax / (6 * 448).
     """
     import torch
-    if not x.is_cuda:
-        raise ValueError("mx_quantize_nvfp4 needs a GPU tensor (libmx has no CPU path)")
-    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_contiguous():
-        raise TypeError("input must be a contiguous bfloat16 or float32 tensor")
+    xdt = _input(x, "mx_quantize_nvfp4")
     b, r, c = _shape3(x.shape)
     out = dict(out or {})
     given = global_scale is not None
     if given:
         out["global_scale"] = global_scale
     planes = _nv_planes(x, axis, out)
+    _check_nv_planes(planes, b, r, c, x.device)
+    _need_gpu(x, "mx_quantize_nvfp4")
     with torch.cuda.device(x.device):
         err = load().mx_quantize_nvfp4(
-            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), AXIS[axis],
+            _ptr(x), xdt, MxShape(b, r, c), AXIS[axis],
             _ptr(planes["global_scale"]), int(given), _ptr(planes.get("row_codes")), _ptr(planes.get("row_scales")),
             _ptr(planes.get("col_codes")), _ptr(planes.get("col_scales")), _stream_of(x))
     if err:
@@ -341,8 +415,15 @@ def mx_dequantize_nvfp4(codes, scales, global_scale, shape, out_dtype: str = "f3
     """Dequantize one NVFP4 plane; ``shape`` is its element shape as stored."""
     import torch
     b, r, c = _shape3(shape)
-    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
-    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=codes.device)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
+    dev = codes.device
+    n = b * r * c
+    _check(codes, "codes", b * r * (c // 2), torch.uint8, dev)
+    _check(scales, "scales", b * r * (c // 16), torch.uint8, dev)
+    _check(global_scale, "global_scale", 4 * b, torch.float32, dev)
+    y = out if out is not None else torch.empty(tuple(shape), dtype=tdt, device=dev)
+    _check(y, "out", n * (2 if out_dtype == "bf16" else 4), tdt, dev)
+    _need_gpu(codes, "mx_dequantize_nvfp4")
     with torch.cuda.device(codes.device):
         err = load().mx_dequantize_nvfp4(_ptr(codes), _ptr(scales), _ptr(global_scale), MxShape(b, r, c),
                                          DTYPE[out_dtype], _ptr(y), _stream_of(codes))
@@ -355,10 +436,12 @@ class BoundQuantizeNvfp4:
     """An mx_quantize_nvfp4 call marshalled once (see BoundQuantize)."""
 
     def __init__(self, x, axis: str, out: dict, global_given: bool = False):
-        import torch
         b, r, c = _shape3(x.shape)
+        xdt = _input(x, "BoundQuantizeNvfp4")
+        _check_nv_planes(out, b, r, c, x.device)
+        _need_gpu(x, "BoundQuantizeNvfp4")
         self._fn = load().mx_quantize_nvfp4
-        self._args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), AXIS[axis],
+        self._args = (_ptr(x), xdt, MxShape(b, r, c), AXIS[axis],
                       _ptr(out["global_scale"]), int(global_given), _ptr(out.get("row_codes")),
                       _ptr(out.get("row_scales")), _ptr(out.get("col_codes")), _ptr(out.get("col_scales")),
                       _stream_of(x))
@@ -388,6 +471,26 @@ def _rq_planes(codes, shape, axis: str, spread: bool, out: dict | None):
     return out
 
 
+def _check_rq_planes(planes: dict, b, r, c, dev) -> None:
+    import torch
+    n = b * r * c
+    nblk = b * (-(-r // 128)) * (-(-c // 128))
+    sizes = {"e4m3": (n, torch.uint8), "e4m3_t": (n, torch.uint8), "block_scale": (4 * nblk, torch.float32),
+             "block_scale_t": (4 * nblk, torch.float32), "spread": (nblk, torch.uint8),
+             "fp4_codes": (b * r * (c // 2), torch.uint8), "fp4_scales": (b * r * (c // 32), torch.uint8)}
+    for k, t in planes.items():
+        if k not in sizes:
+            raise ValueError(f"unknown output plane {k!r}")
+        if t is not None:
+            _check(t, k, sizes[k][0], sizes[k][1], dev)
+
+
+def _check_mxfp4_source(codes, scales, b, r, c) -> None:
+    import torch
+    _check(codes, "codes", b * r * (c // 2), torch.uint8, codes.device)
+    _check(scales, "scales", b * r * (c // 32), torch.uint8, codes.device)
+
+
 def mx_requant_fp4_fp8(codes, scales, shape, axis: str = "row", spread: bool = True, out: dict | None = None):
     """FP4-in-FP8 requantization of an MXFP4 plane (codes [..][R][C/2], scales
     [..][R][C/32] as mx_quantize writes them; ``shape`` is its element shape
@@ -398,11 +501,12 @@ def mx_requant_fp4_fp8(codes, scales, shape, axis: str = "row", spread: bool = T
     and "spread" [..][R'][C'] (largest minus smallest active scale code of each
     128x128 block; the block converted exactly when it is at most 14).
     """
-    if not codes.is_cuda or not scales.is_cuda:
-        raise ValueError("mx_requant_fp4_fp8 needs GPU tensors (libmx has no CPU path)")
     import torch
     b, r, c = _shape3(shape)
+    _check_mxfp4_source(codes, scales, b, r, c)
     planes = _rq_planes(codes, shape, axis, spread, out)
+    _check_rq_planes(planes, b, r, c, codes.device)
+    _need_gpu(codes, "mx_requant_fp4_fp8")
     with torch.cuda.device(codes.device):
         err = load().mx_requant_fp4_fp8(
             _ptr(codes), _ptr(scales), MxShape(b, r, c), AXIS[axis], _ptr(planes.get("e4m3")),
@@ -418,6 +522,9 @@ class BoundRequant:
 
     def __init__(self, codes, scales, shape, axis: str, out: dict):
         b, r, c = _shape3(shape)
+        _check_mxfp4_source(codes, scales, b, r, c)
+        _check_rq_planes(out, b, r, c, codes.device)
+        _need_gpu(codes, "BoundRequant")
         self._fn = load().mx_requant_fp4_fp8
         self._args = (_ptr(codes), _ptr(scales), MxShape(b, r, c), AXIS[axis], _ptr(out.get("e4m3")),
                       _ptr(out.get("block_scale")), _ptr(out.get("e4m3_t")), _ptr(out.get("block_scale_t")),
@@ -437,19 +544,18 @@ def mx_quantize_fp4_fp8(x, mode: str = "floor", axis: str = "both", fp4: bool = 
     one pass. Returns the planes of mx_requant_fp4_fp8 plus, with ``fp4``,
     "fp4_codes" [..][R][C/2] and "fp4_scales" [..][R][C/32]."""
     import torch
-    if not x.is_cuda:
-        raise ValueError("mx_quantize_fp4_fp8 needs a GPU tensor (libmx has no CPU path)")
-    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_contiguous():
-        raise TypeError("input must be a contiguous bfloat16 or float32 tensor")
+    xdt = _input(x, "mx_quantize_fp4_fp8")
     b, r, c = _shape3(x.shape)
     planes = _rq_planes(x, tuple(x.shape), axis, spread, out)
     if fp4:
         lead = (b,) if x.dim() == 3 else ()
         planes.setdefault("fp4_codes", torch.empty(lead + (r, c // 2), dtype=torch.uint8, device=x.device))
         planes.setdefault("fp4_scales", torch.empty(lead + (r, c // 32), dtype=torch.uint8, device=x.device))
+    _check_rq_planes(planes, b, r, c, x.device)
+    _need_gpu(x, "mx_quantize_fp4_fp8")
     with torch.cuda.device(x.device):
         err = load().mx_quantize_fp4_fp8(
-            _ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), MODE[mode], AXIS[axis],
+            _ptr(x), xdt, MxShape(b, r, c), MODE[mode], AXIS[axis],
             _ptr(planes.get("fp4_codes")), _ptr(planes.get("fp4_scales")), _ptr(planes.get("e4m3")),
             _ptr(planes.get("block_scale")), _ptr(planes.get("e4m3_t")), _ptr(planes.get("block_scale_t")),
             _ptr(planes.get("spread")), _stream_of(x))
@@ -462,10 +568,12 @@ class BoundQuantizeFp4Fp8:
     """An mx_quantize_fp4_fp8 call marshalled once (see BoundQuantize)."""
 
     def __init__(self, x, mode: str, axis: str, out: dict):
-        import torch
         b, r, c = _shape3(x.shape)
+        xdt = _input(x, "BoundQuantizeFp4Fp8")
+        _check_rq_planes(out, b, r, c, x.device)
+        _need_gpu(x, "BoundQuantizeFp4Fp8")
         self._fn = load().mx_quantize_fp4_fp8
-        self._args = (_ptr(x), DTYPE["bf16" if x.dtype == torch.bfloat16 else "f32"], MxShape(b, r, c), MODE[mode],
+        self._args = (_ptr(x), xdt, MxShape(b, r, c), MODE[mode],
                       AXIS[axis], _ptr(out.get("fp4_codes")), _ptr(out.get("fp4_scales")), _ptr(out.get("e4m3")),
                       _ptr(out.get("block_scale")), _ptr(out.get("e4m3_t")), _ptr(out.get("block_scale_t")),
                       _ptr(out.get("spread")), _stream_of(x))

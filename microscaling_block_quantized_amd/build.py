@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmx.so")
-SOURCES = ["mx_api.cpp", "mx_cast.hip", "mx_cast_2d.hip", "mx_cast_sr.hip", "mx_dequant.hip", "mx_nvfp4.hip", "mx_requant.hip",
+SOURCES = ["mx_api.cpp", "mx_grid.cpp", "mx_cast.hip", "mx_cast_2d.hip", "mx_cast_sr.hip", "mx_dequant.hip", "mx_nvfp4.hip", "mx_requant.hip",
            "mx_copy.hip"]
 ARCH = "gfx950"
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 
 #include "../../include/libmx.h"
 #include "mx_kernels.h"
@@ -55,7 +56,7 @@ int64_t elements(const mx_shape& s) {
 
 extern "C" {
 
-int mx_version(void) { return 10600; }
+int mx_version(void) { return 10700; }
 
 const char* mx_strerror(int err) {
   switch (err) {
@@ -71,13 +72,16 @@ const char* mx_strerror(int err) {
   }
 }
 
-int mx_plane_bytes(mx_fmt fmt, mx_shape s, size_t* code_bytes, size_t* scale_bytes) {
-  if (!valid_fmt(fmt)) return MX_ERR_ENUM;
+int mx_plane_bytes(mx_fmt fmt, mx_shape s, mx_axis axis, size_t* code_bytes, size_t* scale_bytes) {
+  if (!valid_fmt(fmt) || !valid_axis(axis)) return MX_ERR_ENUM;
   if (code_bytes == nullptr || scale_bytes == nullptr) return MX_ERR_NULL;
   const int64_t n = elements(s);
-  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
-  *code_bytes = size_t(n / 8 * code_bits(fmt));
-  *scale_bytes = size_t(n / kBlock);
+  const bool row = (axis & MX_AXIS_ROW) != 0, col = (axis & MX_AXIS_COL) != 0;
+  if (n < 0 || (row && s.cols % kBlock != 0) || (col && s.rows % kBlock != 0)) return MX_ERR_SHAPE;
+  const int64_t planes = (row ? 1 : 0) + (col ? 1 : 0);
+  // n is a multiple of 32 (one blocked extent is), so both divisions are exact
+  *code_bytes = size_t(planes * (n / 8 * code_bits(fmt)));
+  *scale_bytes = size_t(planes * (n / kBlock));
   return MX_OK;
 }
 
@@ -91,19 +95,32 @@ int mx_quantize(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scal
 int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_scale_mode mode,
                    mx_axis axis, const mx_quant_opts* opts, void* row_codes, uint8_t* row_scales,
                    void* col_codes, uint8_t* col_scales, void* stream) {
-  const mx_quant_opts o = opts ? *opts : mx_quant_opts{MX_ROUND_NEAREST_EVEN, MX_BLOCK_1X32, 0};
+  // The enum fields of a caller's options struct are read as the ints a C
+  // caller stored (any value is legal there; loading an out-of-range value as
+  // a C++ enum would not be).
+  static_assert(sizeof(mx_rounding) == sizeof(int) && sizeof(mx_block) == sizeof(int), "enum fields are ints");
+  int rounding = MX_ROUND_NEAREST_EVEN, block = MX_BLOCK_1X32;
+  uint64_t seed = 0;
+  if (opts != nullptr) {
+    std::memcpy(&rounding, &opts->rounding, sizeof(int));
+    std::memcpy(&block, &opts->block, sizeof(int));
+    seed = opts->seed;
+  }
   if (!valid_fmt(fmt) || !valid_mode(mode) || !valid_dtype(x_dtype) || !valid_axis(axis) ||
-      !valid_rounding(o.rounding) || !valid_block(o.block))
+      !valid_rounding(rounding) || !valid_block(block))
     return MX_ERR_ENUM;
-  const bool b2d = o.block == MX_BLOCK_32X32;
-  const bool sr = o.rounding == MX_ROUND_STOCHASTIC;
+  const bool b2d = block == MX_BLOCK_32X32;
+  const bool sr = rounding == MX_ROUND_STOCHASTIC;
   const bool want_row = (axis & MX_AXIS_ROW) != 0;
   const bool want_col = (axis & MX_AXIS_COL) != 0;
   if (x == nullptr) return MX_ERR_NULL;
   if (want_row != (row_codes != nullptr) || want_row != (row_scales != nullptr)) return MX_ERR_NULL;
   if (want_col != (col_codes != nullptr) || want_col != (col_scales != nullptr)) return MX_ERR_NULL;
   const int64_t n = elements(s);
-  if (n < 0 || s.cols % kBlock != 0) return MX_ERR_SHAPE;
+  // blocked extents are multiples of 32; a column-only cast with 1x32 blocks
+  // blocks no run along cols, which then needs only whole 16-byte row vectors
+  const int64_t col_mult = (want_row || b2d) ? kBlock : (x_dtype == MX_BF16 ? 8 : 4);
+  if (n < 0 || s.cols % col_mult != 0) return MX_ERR_SHAPE;
   if ((want_col || b2d) && s.rows % kBlock != 0) return MX_ERR_SHAPE;
   if (!aligned(x, 16) || (want_row && !aligned(row_codes, 16)) || (want_col && !aligned(col_codes, 16)))
     return MX_ERR_ALIGN;
@@ -138,8 +155,8 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
   a.tiles_r = uint32_t(g.tiles_r);
   a.tiles_c = uint32_t(g.tiles_c);
   a.flags = 0;
-  a.seed_lo = uint32_t(o.seed);
-  a.seed_hi = uint32_t(o.seed >> 32);
+  a.seed_lo = uint32_t(seed);
+  a.seed_hi = uint32_t(seed >> 32);
   // the row-only kernel stores 4 scale bytes of consecutive blocks at once (any cols);
   // the tiled kernel stores the 4 of one row's 128 columns (cols % 128 == 0) or, with
   // 32x32 blocks, of 128 columns in one row of the scale grid (same condition)

@@ -34,6 +34,7 @@
 // non-temporal costs 60%). Tiles are ordered so that each XCD owns a strip of
 // adjacent tile columns and sweeps down the rows.
 #pragma once
+#include "mx_device.h"
 #include "mx_kernels.h"
 #include "mx_sr.h"
 
@@ -41,12 +42,7 @@ namespace mx {
 
 namespace {
 
-constexpr int kWaveRows = 4;                 // waves stacked along rows (32 rows each)
-constexpr int kWaveCols = 2;                 // waves side by side along columns (128 each)
-constexpr int kTileR = 32 * kWaveRows;       // 128
-constexpr int kTileC = 128 * kWaveCols;      // 256
-constexpr int kThreads = 64 * kWaveRows * kWaveCols;
-constexpr int kXcds = 8;
+constexpr int kXcds = 8;                     // tile geometry: mx_enums.h
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -607,8 +603,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // handles 16-byte chunk i of each 1 KiB wave step (4 (BF16) or 8 (FP32) lanes
 // per block); kRowSteps steps per wave are in flight at once. The 4 scale
 // bytes of 4 neighbouring blocks are ORed into one dword store.
-constexpr int kRowThreads = 256;
-constexpr int kRowSteps = 2;
 
 template <bool BF16, int F, int M, int RD>
 __global__ __launch_bounds__(kRowThreads) void mx_cast_rows_kernel(CastArgs a, int64_t nchunks) {
@@ -707,15 +701,13 @@ template <bool BF16, int F, int M, int RD>
 hipError_t launch_rows(const CastArgs& a, int64_t nchunks, hipStream_t s) {
   const int64_t per_block = int64_t(kRowThreads / 64) * 64 * kRowSteps;
   const int64_t blocks = (nchunks + per_block - 1) / per_block;
-  hipLaunchKernelGGL((mx_cast_rows_kernel<BF16, F, M, RD>), dim3(uint32_t(blocks)), dim3(kRowThreads), 0, s, a,
-                     nchunks);
-  return hipGetLastError();
+  return launch_kernel(mx_cast_rows_kernel<BF16, F, M, RD>, dim3(uint32_t(blocks)), dim3(kRowThreads), s, a,
+                       nchunks);
 }
 
 template <bool BF16, int F, int M, int AX, int RD, bool B2>
 hipError_t launch_one(const CastArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((mx_cast_kernel<BF16, F, M, AX, RD, B2>), dim3(nblocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(mx_cast_kernel<BF16, F, M, AX, RD, B2>, dim3(nblocks), dim3(kThreads), s, a);
 }
 
 // Row-only casts with 1x32 blocks are a linear stream (mx_cast_rows_kernel);

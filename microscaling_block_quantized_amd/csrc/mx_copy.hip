@@ -9,7 +9,6 @@ namespace mx {
 namespace {
 
 typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
-constexpr int kCopyThreads = 256;
 
 __global__ __launch_bounds__(kCopyThreads) void copy_nt_kernel(const u32x4c* __restrict__ src, u32x4c* __restrict__ dst,
                                                                int64_t chunks) {
@@ -19,13 +18,10 @@ __global__ __launch_bounds__(kCopyThreads) void copy_nt_kernel(const u32x4c* __r
 
 }  // namespace
 
-int64_t copy_blocks(int64_t bytes) { return (bytes / 16 + kCopyThreads - 1) / kCopyThreads; }
-
 hipError_t launch_copy_nt(const void* src, void* dst, int64_t bytes, hipStream_t s) {
   const int64_t chunks = bytes / 16;
-  hipLaunchKernelGGL(copy_nt_kernel, dim3(uint32_t(copy_blocks(bytes))), dim3(kCopyThreads), 0, s,
-                     static_cast<const u32x4c*>(src), static_cast<u32x4c*>(dst), chunks);
-  return hipGetLastError();
+  return launch_kernel(copy_nt_kernel, dim3(uint32_t(copy_blocks(bytes))), dim3(kCopyThreads), s,
+                       static_cast<const u32x4c*>(src), static_cast<u32x4c*>(dst), chunks);
 }
 
 }  // namespace mx

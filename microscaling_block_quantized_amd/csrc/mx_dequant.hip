@@ -14,13 +14,14 @@
 // One thread handles 16 consecutive elements (half a block): a 16-byte (FP8,
 // INT8), 12-byte (FP6) or 8-byte (E2M1) code load, one scale byte, and 64 or
 // 32 bytes of output.
+#include "mx_device.h"
 #include "mx_kernels.h"
 
 namespace mx {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kDeqThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -99,10 +100,10 @@ __device__ __forceinline__ void decode16(const uint32_t* cw, uint32_t k, float* 
 // B2: 32x32 blocks over rows of `cols` elements; the scale of chunk i (row
 // r = 16 i / cols, column c = 16 i % cols) is scales[(r / 32) * (cols / 32) + c / 32].
 template <int F, bool OUT_BF16, bool B2>
-__global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kDeqThreads) void mx_dequant_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
                                                              void* __restrict__ y, int64_t nchunks, int64_t cols) {
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;   // 16-element chunk
+  const int64_t i = int64_t(blockIdx.x) * kDeqThreads + threadIdx.x;   // 16-element chunk
   if (i >= nchunks) return;
   int64_t si = i >> 1;
   if constexpr (B2) {
@@ -156,10 +157,9 @@ __global__ __launch_bounds__(kThreads) void mx_dequant_kernel(const uint8_t* __r
 template <int F, bool B, bool B2>
 hipError_t launch_dq(const uint8_t* c, const uint8_t* s, void* y, int64_t n, int64_t cols, hipStream_t st) {
   const int64_t chunks = n / 16;
-  const int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((mx_dequant_kernel<F, B, B2>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, c, s, y,
-                     chunks, cols);
-  return hipGetLastError();
+  const int64_t blocks = (chunks + kDeqThreads - 1) / kDeqThreads;
+  return launch_kernel(mx_dequant_kernel<F, B, B2>, dim3(uint32_t(blocks)), dim3(kDeqThreads), st, c, s, y, chunks,
+                       cols);
 }
 
 template <int F>

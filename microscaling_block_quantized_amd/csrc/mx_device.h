@@ -32,11 +32,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace mx {
+#include "mx_enums.h"
 
-enum Fmt : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 2, kE2M3 = 3, kE3M2 = 4, kInt8 = 5 };
-enum Mode : int { kFloor = 0, kRoundUp = 1 };
-enum Axis : int { kRow = 1, kCol = 2, kBoth = 3 };
+namespace mx {
 
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -3,9 +3,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "mx_device.h"
+#include "mx_enums.h"
 
 namespace mx {
+
+template <typename T>
+struct Same {
+  using type = T;
+};
+
+// Launches kernel k and returns the status of this launch itself, as
+// hipLaunchKernel reports it, so an error left behind by an unrelated earlier
+// call is neither reported as this launch's nor cleared. Arguments convert to
+// the kernel's parameter types.
+template <typename... P>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, typename Same<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
+}
 
 // One quantize launch over a dense [batch][rows][cols] tensor.
 struct CastArgs {

@@ -322,8 +322,7 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
 
 template <int SRC, int M, bool ROWS, bool COLS>
 hipError_t launch_rq(const RqArgs& a, uint32_t nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((requant_kernel<SRC, M, ROWS, COLS>), dim3(nblocks), dim3(kRqThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(requant_kernel<SRC, M, ROWS, COLS>, dim3(nblocks), dim3(kRqThreads), s, a);
 }
 
 template <int SRC, int M>

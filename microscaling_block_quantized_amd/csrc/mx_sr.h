@@ -1,7 +1,7 @@
 // Stochastic rounding for the MX cast.
 //
 // "MXFP4 と NVFP4 は何が違うのか調べてみた" §4: the 4-bit pretraining recipe rounds
-// gradients stochastically (and §11 lists stochastic rounding among the P3109
+// gradients stochastically (and §8 lists stochastic rounding among the P3109
 // rounding modes). The rule used here: a scaled value s with |s| < max moves to
 // the grid value above |s| when the fraction f of |s| between its two
 // neighbouring grid values exceeds u / 2^16 for a 16-bit random draw u, and to

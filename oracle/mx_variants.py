@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE, like the rest of ``oracle/``: only the test suite,
 
 What the pages say ([Q] "MXFP4 と NVFP4 は何が違うのか調べてみた", §4, the 4-bit
 pretraining recipe): weights use two-dimensional block scaling, and only
-gradients use stochastic rounding ([Q] §11 adds that the P3109 draft defines
+gradients use stochastic rounding ([Q] §8 adds that the P3109 draft defines
 stochastic rounding among its rounding modes). The pages give neither the
 rounding rule in detail nor a random-number source, so the readings below
 (listed in the design doc) fix them:

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version_and_strerror(lib):
-    assert mxb.mx_version() == 10600
+    assert mxb.mx_version() == 10700
     for code in (MX_OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_ALIAS, E_BIG, E_LAUNCH, -99, 5):
         s = mxb.mx_strerror(code)
         assert isinstance(s, str) and s
@@ -49,22 +49,31 @@ def test_version_and_strerror(lib):
 @pytest.mark.parametrize("fmt,bpe", [("e4m3", 8.25), ("e5m2", 8.25), ("e2m1", 4.25), ("e2m3", 6.25),
                                      ("e3m2", 6.25), ("int8", 8.25)])
 def test_plane_bytes(fmt, bpe):
-    # "MXFP4 と NVFP4 は何が違うのか調べてみた" §2: 4.25 / 6.25 / 8.25 bits per element
-    for shape in [(16384, 4096), (14336, 4096), (64, 4096, 14336), (1, 32)]:
-        cb, sb = mxb.mx_plane_bytes(fmt, shape)
+    # "MXFP4 と NVFP4 は何が違うのか調べてみた" §2: 4.25 / 6.25 / 8.25 bits per element and plane
+    for shape in [(16384, 4096), (14336, 4096), (64, 4096, 14336), (32, 32)]:
         n = 1
         for v in shape:
             n *= v
-        assert (cb + sb) * 8 / n == bpe
-        assert sb == n // 32
+        for axis, planes in (("row", 1), ("col", 1), ("both", 2)):
+            cb, sb = mxb.mx_plane_bytes(fmt, shape, axis)
+            assert (cb + sb) * 8 / n == bpe * planes
+            assert sb == planes * n // 32
 
 
 def test_plane_bytes_errors(lib):
     cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
-    assert lib.mx_plane_bytes(0, MxShape(1, 4, 33), ctypes.byref(cb), ctypes.byref(sb)) == E_SHAPE
-    assert lib.mx_plane_bytes(0, MxShape(0, 4, 32), ctypes.byref(cb), ctypes.byref(sb)) == E_SHAPE
-    assert lib.mx_plane_bytes(7, MxShape(1, 4, 32), ctypes.byref(cb), ctypes.byref(sb)) == E_ENUM
-    assert lib.mx_plane_bytes(0, MxShape(1, 4, 32), None, ctypes.byref(sb)) == E_NULL
+    pb = lambda fmt, shape, axis, c=ctypes.byref(cb), s=ctypes.byref(sb): lib.mx_plane_bytes(fmt, MxShape(*shape),
+                                                                                            axis, c, s)
+    assert pb(0, (1, 4, 33), 1) == E_SHAPE                 # row blocks: cols % 32
+    assert pb(0, (1, 4, 32), 2) == E_SHAPE                 # column blocks: rows % 32
+    assert pb(0, (1, 32, 36), 2) == MX_OK and cb.value == 32 * 36 and sb.value == 36
+    assert pb(0, (1, 4, 32), 1) == MX_OK and cb.value == 128 and sb.value == 4
+    assert pb(2, (2, 64, 32), 3) == MX_OK and cb.value == 2 * 2 * 64 * 16 and sb.value == 2 * 2 * 64
+    assert pb(0, (0, 4, 32), 1) == E_SHAPE
+    assert pb(7, (1, 4, 32), 1) == E_ENUM
+    assert pb(0, (1, 4, 32), 0) == E_ENUM
+    assert pb(0, (1, 4, 32), 4) == E_ENUM
+    assert pb(0, (1, 4, 32), 1, c=None) == E_NULL
 
 
 # Fake, well-aligned, non-overlapping addresses: never dereferenced, because
@@ -89,7 +98,14 @@ def test_quantize_argument_errors(lib):
     assert q(lib, cs=0) == E_NULL
     assert q(lib, axis=1) == E_NULL                    # column pointers must be NULL for row-only
     assert q(lib, axis=1, cc=0, cs=0, shape=(1, 64, 48)) == E_SHAPE
+    assert q(lib, shape=(1, 64, 48)) == E_SHAPE        # row blocks of both copies: cols % 32
     assert q(lib, shape=(1, 48, 64)) == E_SHAPE        # column blocks need rows % 32 == 0
+    # a column-only cast needs whole 16-byte row vectors only: cols % 8 (BF16), cols % 4 (FP32);
+    # accepted shapes are shown by the alias check after the shape check failing
+    assert q(lib, axis=2, rc=0, rs=0, shape=(1, 64, 36)) == E_SHAPE
+    assert q(lib, axis=2, rc=0, rs=0, shape=(1, 64, 40), cc=X + 1024) == E_ALIAS
+    assert q(lib, axis=2, rc=0, rs=0, dt=0, shape=(1, 64, 34)) == E_SHAPE
+    assert q(lib, axis=2, rc=0, rs=0, dt=0, shape=(1, 64, 36), cc=X + 1024) == E_ALIAS
     assert q(lib, shape=(0, 64, 64)) == E_SHAPE
     assert q(lib, shape=(1, -32, 64)) == E_SHAPE
     assert q(lib, shape=(1, 1 << 40, 1 << 40)) == E_SHAPE
@@ -125,6 +141,62 @@ def test_python_binding_rejects_cpu_tensors():
         mxb.mx_quantize(torch.zeros(32, 32, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         mxb.mx_dequantize(torch.zeros(32, dtype=torch.uint8), torch.zeros(1, dtype=torch.uint8), "e4m3", (1, 32))
+
+
+def test_python_binding_checks_every_buffer():
+    """The binding checks each tensor against the sizes its shape and format
+    imply before anything reaches the C ABI (which trusts them). With CPU
+    tensors, a correct set of buffers gets as far as the GPU check."""
+    import torch
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+
+    def raises(fn, text):
+        with pytest.raises(ValueError) as e:
+            fn()
+        assert text in str(e.value), str(e.value)
+    gpu = "needs GPU"
+    x = torch.zeros((64, 64), dtype=torch.bfloat16)
+    # mx_quantize: caller-given planes
+    ok = {"row_codes": u8(4096), "row_scales": u8(128), "col_codes": u8(4096), "col_scales": u8(128)}
+    raises(lambda: mxb.mx_quantize(x, "e4m3", out=ok), gpu)
+    raises(lambda: mxb.mx_quantize(x, "e4m3", out=dict(ok, row_codes=u8(4095))), "row_codes holds 4095")
+    raises(lambda: mxb.mx_quantize(x, "e2m1", out=dict(ok)), "row_codes holds 4096")     # E2M1 needs 2048
+    raises(lambda: mxb.mx_quantize(x, "e4m3", out=dict(ok, col_scales=f32(32))), "dtype")
+    raises(lambda: mxb.mx_quantize(x, "e4m3", out=dict(ok, col_codes=u8(8192)[::2])), "contiguous")
+    raises(lambda: mxb.mx_quantize(x, "e4m3", block="32x32", out=dict(ok)), "row_scales holds 128")
+    raises(lambda: mxb.mx_quantize(x.to(torch.float16)), "bfloat16 or float32")
+    raises(lambda: mxb.mx_quantize(x.t()), "contiguous")
+    # mx_dequantize
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(128), "e4m3", (64, 64)), gpu)
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(127), "e4m3", (64, 64)), "scales holds 127")
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(128), "e2m1", (64, 64)), "codes holds 4096")
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(128), "e4m3", (64, 64), "f32", out=f32(4095)), "out holds")
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(128), "e4m3", (64, 64), "f32",
+                                     out=torch.zeros(4096, dtype=torch.bfloat16)), "dtype")
+    raises(lambda: mxb.mx_dequantize(u8(4096), u8(4), "e4m3", (64, 64), block="32x32"), gpu)
+    raises(lambda: mxb.BoundDequantize(u8(4096), u8(128), "e4m3", (64, 64), f32(4000)), "y holds")
+    raises(lambda: mxb.BoundQuantize(x, "e4m3", "floor", "row", {"row_codes": u8(4096)}), "exactly")
+    raises(lambda: mxb.BoundQuantize(x, "e4m3", "floor", "row", {"row_codes": u8(4096), "row_scales": u8(64)}),
+           "row_scales holds 64")
+    # NVFP4
+    nv = {"global_scale": f32(1), "row_codes": u8(2048), "row_scales": u8(256), "col_codes": u8(2048),
+          "col_scales": u8(256)}
+    raises(lambda: mxb.mx_quantize_nvfp4(x, out=dict(nv)), gpu)
+    raises(lambda: mxb.mx_quantize_nvfp4(x, out=dict(nv, row_scales=u8(128))), "row_scales holds 128")
+    raises(lambda: mxb.mx_quantize_nvfp4(x, global_scale=f32(2), out=dict(nv)), "global_scale holds 8")
+    raises(lambda: mxb.mx_dequantize_nvfp4(u8(2048), u8(256), f32(1), (64, 64)), gpu)
+    raises(lambda: mxb.mx_dequantize_nvfp4(u8(2048), u8(256), u8(4), (64, 64)), "dtype")
+    raises(lambda: mxb.mx_dequantize_nvfp4(u8(2048), u8(255), f32(1), (64, 64)), "scales holds 255")
+    # FP4-in-FP8 requantization and the one-pass QAT step
+    rq = {"e4m3": u8(4096), "block_scale": f32(1), "e4m3_t": u8(4096), "block_scale_t": f32(1), "spread": u8(1)}
+    raises(lambda: mxb.mx_requant_fp4_fp8(u8(2048), u8(128), (64, 64), "both", out=dict(rq)), gpu)
+    raises(lambda: mxb.mx_requant_fp4_fp8(u8(2048), u8(64), (64, 64), "both", out=dict(rq)), "scales holds 64")
+    raises(lambda: mxb.mx_requant_fp4_fp8(u8(2048), u8(128), (64, 64), "both", out=dict(rq, block_scale=f32(2))),
+           "block_scale holds 8")
+    raises(lambda: mxb.mx_quantize_fp4_fp8(x, out=dict(rq, fp4_codes=u8(2047))), "fp4_codes holds 2047")
+    raises(lambda: mxb.mx_quantize_fp4_fp8(x, out=dict(rq, e4m3_t=u8(4096).view(64, 64).t())), "contiguous")
+    raises(lambda: mxb.mx_quantize_fp4_fp8(x, out=dict(rq)), gpu)
 
 
 def qx(lib, opts=None, x=X, dt=1, shape=(1, 64, 64), fmt=0, mode=0, axis=3, rc=RC, rs=RS, cc=CC, cs=CS):
@@ -280,8 +352,10 @@ def test_header_is_plain_c(tmp_path):
         "int main(void) {\n"
         "  mx_shape s = {1, 32, 64};\n"
         "  size_t code = 0, scale = 0;\n"
-        "  if (mx_plane_bytes(MX_E2M1, s, &code, &scale) != MX_OK) return 1;\n"
+        "  if (mx_plane_bytes(MX_E2M1, s, MX_AXIS_ROW, &code, &scale) != MX_OK) return 1;\n"
         "  if (code != 1024 || scale != 64) return 2;\n"
+        "  if (mx_plane_bytes(MX_E4M3, s, MX_AXIS_BOTH, &code, &scale) != MX_OK) return 5;\n"
+        "  if (code != 4096 || scale != 128) return 6;\n"
         "  if (mx_quantize(0, MX_BF16, s, MX_E4M3, MX_SCALE_FLOOR, MX_AXIS_BOTH, 0, 0, 0, 0, 0) != MX_ERR_NULL) return 3;\n"
         "  if (mx_copy_nt(0, 0, 16, 0) != MX_ERR_NULL) return 4;\n"
         "  return mx_strerror(MX_ERR_ALIGN)[0] == 0;\n"

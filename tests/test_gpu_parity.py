@@ -210,6 +210,32 @@ def test_fp6_row_lines(mx, fmt, dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_column_only_any_vector_width(mx, fmt, dt):
+    """A column-only cast blocks no run along cols, so cols need only fill whole
+    16-byte vectors (8 BF16 or 4 FP32): cols of 40, 36, 264 and 300 (a ragged
+    last tile) with outputs that start as a sentinel and a guard band after
+    each plane, batches, both scale rules."""
+    g = torch.Generator().manual_seed(36)
+    step = 8 if dt == "bf16" else 4
+    bits = OFMT[fmt].bits
+    for b, r, c in [(1, 64, 40), (2, 96, 8 * 37 if dt == "bf16" else 36), (1, 160, 264), (3, 32, 8 * 38 if dt == "bf16" else 300)]:
+        assert c % step == 0
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-8, 8, (b, 1, c), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
+        for mode in MODES:
+            nc, ns = b * c * r * bits // 8, b * c * (r // 32)
+            cc = torch.full((nc + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+            cs = torch.full((ns + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+            got = mx.mx_quantize(x.cuda(), fmt, mode, "col", out={"col_codes": cc[:nc].view(b, c, r * bits // 8),
+                                                                  "col_scales": cs[:ns].view(b, c, r // 32)})
+            torch.cuda.synchronize()
+            assert_same({k: v.cpu().numpy() for k, v in got.items()}, oracle_quant(x, fmt, mode, "col"),
+                        f"col-only {(b, r, c)} {mode}")
+            assert (cc[nc:].cpu() == 0xA5).all() and (cs[ns:].cpu() == 0xA5).all()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "int8"])
 def test_staggered_strip_order(mx, fmt, dt):
     """8192-row slices give column-plane pitches of 8 or 4 KiB and 64 tile rows,
