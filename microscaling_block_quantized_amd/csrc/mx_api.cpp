@@ -349,6 +349,9 @@ static int rq_launch(int src, int mode, const void* x, const void* codes, const 
   // single copy
   if (src == mx::kFromMx && want_row && want_col && s.cols % 256 == 0 && aligned(scales, 4))
     a.flags |= mx::kRqScaleWords;
+  // tile rows owned by one XCD each (the scale plane's lines then reach one L2):
+  // measured 30.64 -> 30.34 us for 14336x4096 with both copies
+  if (src == mx::kFromMx && (s.batch * tiles_r) % 8 == 0) a.flags |= mx::kRqXcdRows;
   const hipError_t e = mx::launch_requant(src, mode, int(axis), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

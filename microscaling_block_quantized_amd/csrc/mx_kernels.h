@@ -116,6 +116,10 @@ struct RqArgs {
 // (every tile full width) and a 4-byte-aligned scale plane: each thread loads
 // one dword of its tile's scales (tile row t / 2, bytes 4 (t & 1) .. +3) into LDS.
 constexpr uint32_t kRqScaleWords = 1u;
+// XCD x (workgroup % 8) takes tile rows x, x + 8, ... (all tiles of each), so
+// each 128-byte line of the scale plane is fetched into one XCD's L2 instead
+// of all eight. Set when batch * tiles_r is a multiple of 8.
+constexpr uint32_t kRqXcdRows = 2u;
 enum RqSource : int { kFromMx = 0, kFromBf16 = 1, kFromF32 = 2 };
 // mode: the MXFP4 scale rule (kFloor / kRoundUp) when casting from x.
 hipError_t launch_requant(int src, int mode, int axis, const RqArgs& a, hipStream_t s);

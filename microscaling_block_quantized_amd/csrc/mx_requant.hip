@@ -131,10 +131,22 @@ __global__ __launch_bounds__(kRqThreads) void requant_kernel(RqArgs a) {
   // the tile's 128 x 8 scale bytes, loaded as one dword per thread (kRqScaleWords)
   __shared__ __attribute__((aligned(4))) uint8_t lds_k[SRC == kFromMx ? kRqRows * 8 : 4];
 
-  const uint32_t per_slice = a.tiles_r * a.tiles_c;
-  const uint32_t bi = blockIdx.x / per_slice;
-  const uint32_t rem = blockIdx.x % per_slice;
-  const uint32_t tr = rem / a.tiles_c, tc = rem % a.tiles_c;
+  uint32_t bi, tr, tc;
+  if (a.flags & kRqXcdRows) {
+    // workgroup w runs on XCD w % 8: XCD x walks tile rows x, x + 8, ..., all
+    // tile columns of each before the next (batch * tiles_r % 8 == 0)
+    const uint32_t xcd = blockIdx.x % 8u, idx = blockIdx.x / 8u;
+    const uint32_t rowi = (idx / a.tiles_c) * 8u + xcd;
+    tc = idx % a.tiles_c;
+    bi = rowi / a.tiles_r;
+    tr = rowi - bi * a.tiles_r;
+  } else {
+    const uint32_t per_slice = a.tiles_r * a.tiles_c;
+    bi = blockIdx.x / per_slice;
+    const uint32_t rem = blockIdx.x % per_slice;
+    tr = rem / a.tiles_c;
+    tc = rem % a.tiles_c;
+  }
   const int64_t R = a.rows, C = a.cols;
   const int64_t r0 = int64_t(tr) * kRqRows, c0 = int64_t(tc) * kRqCols;
   const int rows_in = int(min<int64_t>(R - r0, kRqRows));

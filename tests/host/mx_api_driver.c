@@ -164,6 +164,12 @@ int main(void) {
     const mx_shape r40 = {1, 40, 64};
     CHECK(mx_requant_fp4_fp8(A(1), B(2), s, MX_AXIS_BOTH, B(3), F(4), B(5), F(6), B(7), 0) == MX_OK);
     CHECK(stub_rq_tiles_r() == 2 && stub_rq_tiles_c() == 2 && stub_rq_total() == 4 && (stub_rq_flags() & stub_flag(5)));
+    CHECK(!(stub_rq_flags() & stub_flag(6)));
+    {
+      const mx_shape b4 = {4, 256, 512};
+      CHECK(mx_requant_fp4_fp8(A(1), B(2), b4, MX_AXIS_BOTH, B(3), F(4), B(5), F(6), B(7), 0) == MX_OK);
+      CHECK(stub_rq_total() == 16 && (stub_rq_flags() & stub_flag(6)));
+    }
     CHECK(mx_requant_fp4_fp8(A(1), B(2), s, (mx_axis)5, B(3), F(4), B(5), F(6), B(7), 0) == MX_ERR_ENUM);
     CHECK(mx_requant_fp4_fp8(A(1), NULL, s, MX_AXIS_BOTH, B(3), F(4), B(5), F(6), B(7), 0) == MX_ERR_NULL);
     CHECK(mx_requant_fp4_fp8(A(1), B(2), r40, MX_AXIS_BOTH, B(3), F(4), B(5), F(6), B(7), 0) == MX_ERR_SHAPE);

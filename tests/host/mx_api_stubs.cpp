@@ -78,7 +78,8 @@ unsigned stub_flag(int which) {
     case 2: return mx::kStaggerStrips;
     case 3: return mx::kRowScaleQword;
     case 4: return mx::kNvMarkedAmax;
-    default: return mx::kRqScaleWords;
+    case 5: return mx::kRqScaleWords;
+    default: return mx::kRqXcdRows;
   }
 }
 }

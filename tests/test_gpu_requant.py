@@ -76,6 +76,31 @@ def test_scale_words_batches_and_ragged_rows(mx):
         check(mx, codes, scales, "both", f"{(b, r, c)}")
 
 
+@pytest.mark.parametrize("axis", ["row", "col", "both"])
+def test_xcd_tile_row_order(mx, axis):
+    """When batch * ceil(rows / 128) is a multiple of 8, each XCD takes whole tile
+    rows (tile row t on XCD t mod 8): batches, ragged last tile rows and columns,
+    narrow tensors, outputs that start as a sentinel (a tile left unwritten or
+    written twice to the wrong place shows up)."""
+    rng = np.random.default_rng(75)
+    for b, r, c in [(2, 512, 4128), (8, 112, 256), (1, 1024, 96), (4, 272, 544), (2, 4096, 512)]:
+        codes, scales = plane(rng, b, r, c, 100, 12, nan_frac=0.002)
+        nbr, nbc = -(-r // 128), -(-c // 128)
+        out = {}
+        if axis in ("row", "both"):
+            out["e4m3"] = torch.full((b, r, c), 0xA5, dtype=torch.uint8, device="cuda")
+            out["block_scale"] = torch.full((b, nbr, nbc), -1.0, dtype=torch.float32, device="cuda")
+        if axis in ("col", "both"):
+            out["e4m3_t"] = torch.full((b, c, r), 0xA5, dtype=torch.uint8, device="cuda")
+            out["block_scale_t"] = torch.full((b, nbc, nbr), -1.0, dtype=torch.float32, device="cuda")
+        out["spread"] = torch.full((b, nbr, nbc), 0xA5, dtype=torch.uint8, device="cuda")
+        got = mx.mx_requant_fp4_fp8(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), (b, r, c), axis,
+                                    out=out)
+        torch.cuda.synchronize()
+        compare({k: v.cpu().numpy() for k, v in got.items()}, O.requant_fp4_to_fp8(codes, scales), axis,
+                f"{(b, r, c)}")
+
+
 def test_row_copy_accepts_any_row_count(mx):
     rng = np.random.default_rng(72)
     for r in (1, 37, 129, 255):
