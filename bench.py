@@ -448,15 +448,22 @@ def summarize_trace(stats_csv: str, command: str, workload: str) -> str:
     return "\n".join(out) + "\n"
 
 
+CALIBRATION_COPIES = 30      # the timed torch copies of known size at the end of every bench run
+
+
 def _counter_means(path, counter, keys):
+    """Mean counter value per kernel. For torch's copy kernel only the last
+    CALIBRATION_COPIES dispatches count: those are the bench's own copies of a
+    known size (input set-up makes other, smaller copies earlier in the run)."""
     acc = {}
-    for r in _csv_rows(path):
-        if r["Counter_Name"] != counter:
-            continue
+    rows = sorted((r for r in _csv_rows(path) if r["Counter_Name"] == counter), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
         for sub_, key in keys:
             if sub_ in r["Kernel_Name"]:
                 acc.setdefault(key, []).append(float(r["Counter_Value"]))
                 break
+    if "copy" in acc:
+        acc["copy"] = acc["copy"][-CALIBRATION_COPIES:]
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
