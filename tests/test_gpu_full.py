@@ -127,3 +127,107 @@ def test_whole_activations_nvfp4(mx):
                        {"col_codes": Fraction(1, 2), "col_scales": Fraction(1, 16)})
     assert n == 32
     assert not bad, bad[:5]
+
+
+# ---------------- the variants at full size ----------------
+
+SR_SEED = 0x123456789ABCDEF0           # high key bits set
+
+
+def test_whole_gradients_sr_e2m1_col(mx):
+    """8192x8192 FP32 gradients to E2M1 columns with stochastic rounding (round-up
+    scale rule): every code and scale, each slab drawing its bits at its flat
+    offset in the tensor."""
+    R = C = 8192
+    x = I.gradients(R, C, seed=3, device="cuda")
+    out = mx.mx_quantize(x, "e2m1", "roundup", "col", rounding="sr", seed=SR_SEED)
+    torch.cuda.synchronize()
+    got = host(out, batched=False)
+    xb = I.to_bits(x)[None]
+    del out, x
+
+    def oracle(xs, bi, r0):
+        return O.quantize_ex(xs, "f32", O.E2M1, O.ROUNDUP, O.COL, rounding=O.SR, seed=SR_SEED, first=r0 * C)
+    bad, n = W.compare(xb, oracle, got, mx_cols("e2m1"), with_offset=True)
+    assert n == 16
+    assert not bad, bad[:5]
+
+
+def test_whole_weights_2d_e2m1(mx):
+    """14336x4096 BF16 weights to E2M1 with 32x32 blocks, both copies: every
+    code and every scale of both scale grids."""
+    x = I.weights(14336, 4096, seed=2, device="cuda")
+    out = mx.mx_quantize(x, "e2m1", "floor", "both", block="32x32")
+    torch.cuda.synchronize()
+    got = host(out, batched=False)
+    xb = I.to_bits(x)[None]
+    del out, x
+    bad, n = W.compare(xb, lambda xs: O.quantize_ex(xs, "bf16", O.E2M1, O.FLOOR, O.BOTH, block=O.BLOCK_32X32), got,
+                       mx_cols("e2m1"), cut={"row_scales": ("row", Fraction(1, 32))})
+    assert n == 28
+    assert not bad, bad[:5]
+
+
+FP8_CUT = {"e4m3": ("row", Fraction(1)), "block_scale": ("row", Fraction(1, 128)),
+           "spread": ("row", Fraction(1, 128)), "e4m3_t": ("col", Fraction(1)),
+           "block_scale_t": ("col", Fraction(1, 128)), "fp4_codes": ("row", Fraction(1)),
+           "fp4_scales": ("row", Fraction(1))}
+
+
+def fp8_host(out: dict) -> dict:
+    """Planes to host memory, FP32 block scales as their bit patterns."""
+    got = {k: v.cpu().numpy()[None] for k, v in out.items()}
+    for k in ("block_scale", "block_scale_t"):
+        if k in got:
+            got[k] = got[k].view(np.uint32)
+    return got
+
+
+def fp8_bits(exp: dict) -> dict:
+    exp = dict(exp)
+    for k in ("block_scale", "block_scale_t"):
+        exp[k] = np.asarray(exp[k], dtype=np.float32).view(np.uint32)
+    return exp
+
+
+def test_whole_fp4_in_fp8_requant(mx):
+    """14336x4096 weights: the MXFP4 plane (floor rule) requantized to FP8 with
+    128x128 block scales, as the benchmark runs it: every code of both copies,
+    every block scale (as bits) and every spread. The slabs of 512 rows are 4
+    block rows; the oracle gets the same MXFP4 plane the kernel read."""
+    R, C = 14336, 4096
+    w = I.weights(R, C, seed=2, device="cuda")
+    q = mx.mx_quantize(w, "e2m1", "floor", "row")
+    out = mx.mx_requant_fp4_fp8(q["row_codes"], q["row_scales"], (R, C), "both")
+    torch.cuda.synchronize()
+    got = fp8_host(out)
+    src = np.concatenate([q["row_codes"].cpu().numpy(), q["row_scales"].cpu().numpy()], axis=1)[None]
+    del out, q, w
+
+    def oracle(xs):
+        return fp8_bits(O.requant_fp4_to_fp8(xs[None, :, :C // 2], xs[None, :, C // 2:]))
+    bad, n = W.compare(src, oracle, got, {}, cut=FP8_CUT)
+    assert n == 28
+    assert not bad, bad[:5]
+
+
+def test_whole_qat_fp32_master(mx):
+    """14336x4096 FP32 master weights through MXFP4 (floor rule) to both FP8
+    copies in one pass: the MXFP4 plane, both FP8 copies, block scales and
+    spreads, all against the oracle's quantize followed by its requantization."""
+    R, C = 14336, 4096
+    x = I.weights(R, C, seed=2, device="cuda").float()
+    out = mx.mx_quantize_fp4_fp8(x, "floor", "both")
+    torch.cuda.synchronize()
+    got = fp8_host(out)
+    xb = I.to_bits(x)[None]
+    del out, x
+
+    def oracle(xs):
+        q = O.quantize(xs, "f32", O.E2M1, O.FLOOR, O.ROW)
+        exp = fp8_bits(O.requant_fp4_to_fp8(q["row_codes"], q["row_scales"]))
+        exp["fp4_codes"], exp["fp4_scales"] = q["row_codes"], q["row_scales"]
+        return exp
+    bad, n = W.compare(xb, oracle, got, {}, cut=FP8_CUT)
+    assert n == 28
+    assert not bad, bad[:5]

@@ -40,3 +40,31 @@ def test_finds_nothing_then_every_planted_byte(fmt):
         assert len(bad) == 1 and bad[0][0] == k and bad[0][1] == 2 and bad[0][3] == 1, (k, bad)
         # the row planes put it in the last slab; the column planes in the slab of the last rows
         assert bad[0][2] == 64
+
+
+def test_block_grids_and_slab_offsets():
+    """32x32-block scale grids cut by ("row", 1/32) and ("col", 1/32), and an
+    oracle that needs the slab's position (stochastic rounding draws follow the
+    flat element index): the whole-tensor planes match slab by slab, and one
+    planted byte in the row scale grid is found in its slab."""
+    b, r, c = 2, 128, 96
+    x = _data(b, r, c, 2)
+    seed = 0x1234_5678_9ABC
+    whole = [O.quantize_ex(x[i], "f32", O.E2M1, O.ROUNDUP, O.BOTH, rounding=O.SR, seed=seed, block=O.BLOCK_32X32,
+                           first=i * r * c) for i in range(b)]
+    got = {k: np.concatenate([w[k] for w in whole]) for k in whole[0]}
+    col = {"col_codes": Fraction(1, 2), "col_scales": Fraction(1, 32)}
+    cut = {"row_scales": ("row", Fraction(1, 32))}
+
+    def oracle(xs, bi, r0):
+        return O.quantize_ex(xs, "f32", O.E2M1, O.ROUNDUP, O.BOTH, rounding=O.SR, seed=seed, block=O.BLOCK_32X32,
+                             first=(bi * r + r0) * c)
+    bad, n = W.compare(x, oracle, got, col, slab=64, cut=cut, with_offset=True)
+    assert n == b * 2 and bad == []
+    got["row_scales"][1, 3, 0] ^= 1                          # tile row 3 of slice 1: rows 96..127
+    bad, _ = W.compare(x, oracle, got, col, slab=64, cut=cut, with_offset=True)
+    assert [(k, bi, r0) for k, bi, r0, *_ in bad] == [("row_scales", 1, 64)]
+    # an oracle that ignored the offset would draw the wrong bits
+    bad, _ = W.compare(x, lambda xs: O.quantize_ex(xs, "f32", O.E2M1, O.ROUNDUP, O.BOTH, rounding=O.SR, seed=seed,
+                                                     block=O.BLOCK_32X32), got, col, slab=64, cut=cut)
+    assert bad
