@@ -27,25 +27,28 @@
 //  * Block code: estimated as fp32(amax_b * k), k = fp32(fp32(1/6) * fp32(1/g)),
 //    within 4 FP32 ulps of the exact amax_b / (6 g) while amax_b >= 2^-120 and
 //    2^-125 <= g <= 2^100. E4M3 rounding is monotone: when t - 16 ulps and
-//    t + 16 ulps round to the same code, that is the code of the exact quotient.
-//    Any other block compares amax_b with (midpoint x 6 g) in FP64, which is
-//    exact (at most 5 + 2 + 24 significant bits).
+//    t + 16 ulps round to the same code, that is the code of the exact quotient
+//    (t is first capped at 448: every quotient above it saturates to 448, and
+//    the window then stays below E4M3's overflow). Any other block compares
+//    amax_b with (midpoint x 6 g) in FP64, which is exact (at most 5 + 2 + 24
+//    significant bits).
 //  * Elements: r_b = fp32(1 / fp32(s_b g)) depends only on the block code, so
 //    each workgroup divides once per code (256 entries in LDS). q' = fp32(x r_b)
 //    is within 3 FP32 ulps of the exact quotient Q = x / (s_b g), which is not
 //    enough near an E2M1 midpoint, and with BF16 inputs Q lands next to short
 //    binary values often (g = fp32(A / 2688) has a periodic significand). So
 //    every element is decided exactly, without a branch, on magnitudes: m = the
-//    E4M3 value nearest to min(|q'|, 8) (one paired conversion there and back).
+//    E4M3 value nearest to min(|q'|, 8) (the product clamped to [0, 1] with r_b
+//    / 8, then one paired conversion dividing by 2^-3, and one back).
 //    All E2M1 values and midpoints are E4M3 values, so when m is not a midpoint
 //    |q'| and m round alike. sigma = fma(-(m s_b), g, |x|) has the exact sign
 //    of |Q| - m (m s_b has at most 8 significant bits, and for
 //    2^-90 <= g <= 2^100 a nonzero |x| - m s_b g is at least 2^-149 in
-//    magnitude, so the one rounding keeps it nonzero). m moved by up to 2^-10
+//    magnitude, so the one rounding keeps it nonzero). m moved by one FP32 ulp
 //    towards |Q| (not at all when sigma is 0, an exact tie), with the sign of x,
-//    then takes the hardware E2M1 rounding, which is the exact code: the move
-//    is more than an FP32 ulp of m when m is a midpoint and less than m's
-//    distance to any other rounding boundary. With g outside that range every element compares
+//    then takes the hardware E2M1 rounding, which is the exact code: one ulp
+//    above or below a midpoint rounds away from it, and an m that is not a
+//    midpoint is a whole E4M3 step from every rounding boundary. With g outside that range every element compares
 //    |x| with (midpoint x s_b g) in FP64 instead (exact: 3 + 4 + 24 bits).
 #include "mx_cast_impl.h"
 
@@ -56,13 +59,9 @@ namespace {
 constexpr float kNvGlobalDiv = 6.0f * 448.0f;      // 2688
 constexpr float kRcp6 = 0x1.555556p-3f;            // fp32(1/6)
 constexpr uint32_t kNvWindow = 16;                 // ulps each side of the estimate
-constexpr uint32_t kNvTcap = 0x49800000u;          // 2^20: every t above 464 saturates alike
+constexpr uint32_t kNvTcap = 0x43E00000u;          // 448: every t above it saturates alike, and
+                                                   // 448 + 16 ulps stays below E4M3's overflow at 464
 constexpr uint32_t kNvAmin = 0x03800000u;          // 2^-120: amax/6 stays a normal FP32
-// Element decision: sigma * (r_b * 2^24) moves m by at least 2^-12 when sigma
-// is not 0 (a nonzero sigma is at least 2^-34 |x|, and m >= 0.25 at a midpoint),
-// and the move is clamped to 2^-10.
-constexpr float kNvNudgeGain = 0x1p24f;
-constexpr float kNvNudge = 0x1p-10f;
 // global scales for which the element decision above is exact
 constexpr float kNvGmin = 0x1p-90f, kNvGmax = 0x1p100f;
 
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(kAmaxThreads) void nv_amax_kernel(const uint8_t* __
 
 struct NvBlock {
   uint32_t code;     // UE4M3 byte
-  float rcp;         // 1 / (s_b * g)
+  float rcp8;        // 1 / (8 s_b g): r_b / 8, exact (a power-of-two step)
   bool zero;         // store codes 0
 };
 
@@ -187,28 +186,31 @@ __device__ __forceinline__ uint32_t nv_code_exact(uint32_t amag, float g) {
 }
 
 // The same code through the estimate, falling back to nv_code_exact.
+// A zero block (amag 0) estimates t = 0 and codes 0 through the same window;
+// NaN / Inf blocks (amag >= 0x7F800000) take 0x7F.
 __device__ __forceinline__ uint32_t nv_code(uint32_t amag, const NvScale& s) {
   const uint32_t tb = min(__float_as_uint(__uint_as_float(amag) * s.k), kNvTcap);
   const uint32_t lo = tb > kNvWindow ? tb - kNvWindow : 0u;
-  const uint32_t w = cvt2_f32<kE4M3, false>(0u, __uint_as_float(lo), __uint_as_float(tb + kNvWindow),
+  const uint32_t w = cvt2_f32<kE4M3, false>(tb, __uint_as_float(lo), __uint_as_float(tb + kNvWindow),
                                             scale_operand(127u));
-  const uint32_t c0 = min(w & 0xFFu, 0x7Eu), c1 = min((w >> 8) & 0xFFu, 0x7Eu);
-  uint32_t c = c0;
-  bool slow = !(s.fast && amag >= kNvAmin && c0 == c1);
-  if (amag == 0u && s.fast) { c = 0u; slow = false; }
-  if (amag >= 0x7F800000u) { c = 0x7Fu; slow = false; }
+  const uint32_t c0 = w & 0xFFu, c1 = (w >> 8) & 0xFFu;
+  const bool special = amag >= 0x7F800000u;
+  // fast: amag == 0 or amag >= 2^-120 (one unsigned compare), and both ends agree
+  const bool slow = !special && !(s.fast && amag - 1u >= kNvAmin - 1u && c0 == c1);
+  uint32_t c = special ? 0x7Fu : c0;
   if (slow) c = nv_code_exact(amag, s.g);
   return c;
 }
 
-// LDS table of 1 / fp32(s_c * g) for every scale byte c (g in [2^-90, 2^100]);
+// LDS table of fp32(1 / fp32(s_c * g)) / 8 for every scale byte c (g in
+// [2^-90, 2^100], so the quotient stays normal and the division by 8 is exact);
 // NaN marks the codes whose blocks store codes 0 (c == 0 and the NaN code 0x7F).
 constexpr int kNvTab = 256;
 __device__ __forceinline__ void nv_fill_table(float* tab, float g) {
   const int c = threadIdx.x;
   if (c < kNvTab) {
     const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uint32_t(c), scale_operand(127u), false)[0];
-    const float r = 1.0f / (s * g);
+    const float r = (1.0f / (s * g)) * 0.125f;
     tab[c] = (c == 0 || c == 0x7F) ? __builtin_nanf("") : r;
   }
 }
@@ -216,8 +218,8 @@ __device__ __forceinline__ void nv_fill_table(float* tab, float g) {
 __device__ __forceinline__ NvBlock nv_block(uint32_t amag, const NvScale& s, const float* tab) {
   NvBlock b;
   b.code = nv_code(amag, s);
-  b.rcp = tab[b.code];
-  b.zero = b.rcp != b.rcp;
+  b.rcp8 = tab[b.code];
+  b.zero = b.rcp8 != b.rcp8;
   return b;
 }
 
@@ -242,13 +244,20 @@ __device__ __forceinline__ uint32_t nv_code1_exact(float f, double d) {
 }
 
 // One element's exactly rounded quotient stand-in (see the header), worked on
-// magnitudes: m, the E4M3 value nearest to min(|q'|, 8), moved by at most 2^-10
-// towards |x| / (s_b g), kept at least 2^-100 (no subnormal reaches the
-// conversion), and given the sign of x (so that -0 and tiny negative x code as -0).
-__device__ __forceinline__ float nv_nudged(float f, float m, float ms, float g, float gain) {
+// magnitudes: m, the E4M3 value nearest to min(|q'|, 8), moved by one FP32 ulp
+// towards |x| / (s_b g) (not at all at an exact tie), then given the sign of x
+// (so that -0 and tiny negative x code as -0; the E2M1 conversion keeps the
+// sign of zero and subnormal inputs). sigma is never -0: the sum of |x| and a
+// product of sign <= 0 that is exactly zero rounds to +0, so its bits read as
+// an integer are positive for sigma > 0, 0 for a tie and negative for sigma < 0.
+// m = 0 only moves up (to the smallest subnormal, which codes as 0).
+__device__ __forceinline__ float nv_nudged(float f, float m, float ms, float g) {
   const float sigma = __builtin_fmaf(-ms, g, __builtin_fabsf(f));   // exact sign of |x| - m s_b g
-  const float mag = __builtin_fmaxf(m + __builtin_amdgcn_fmed3f(sigma * gain, -kNvNudge, kNvNudge), 0x1p-100f);
-  return __builtin_copysignf(mag, f);
+  // clamp of sigma's bits to [-1, 1] as one v_med3_i32 (written out: the compiler
+  // turns the min / max form into two compares and two selects)
+  int step;
+  asm("v_med3_i32 %0, %1, -1, 1" : "=v"(step) : "v"(sigma));
+  return __builtin_copysignf(__uint_as_float(__float_as_uint(m) + uint32_t(step)), f);
 }
 
 // Four FP32 values -> four E2M1 codes in the low 16 bits, each the exact
@@ -256,22 +265,23 @@ __device__ __forceinline__ float nv_nudged(float f, float m, float ms, float g, 
 __device__ __forceinline__ uint32_t nv_encode4(float f0, float f1, float f2, float f3, const NvBlock& b,
                                                float g) {
   const float one = scale_operand(127u);
-  {
-    const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.code, one, false)[0];
-    const float gain = b.rcp * kNvNudgeGain;
-    const float q0 = __builtin_fminf(__builtin_fabsf(f0) * b.rcp, 8.0f);
-    const float q1 = __builtin_fminf(__builtin_fabsf(f1) * b.rcp, 8.0f);
-    const float q2 = __builtin_fminf(__builtin_fabsf(f2) * b.rcp, 8.0f);
-    const float q3 = __builtin_fminf(__builtin_fabsf(f3) * b.rcp, 8.0f);
-    uint32_t e = cvt2_f32<kE4M3, false>(0u, q0, q1, one);       // nearest E4M3 values (no overflow at 8)
-    e = cvt2_f32<kE4M3, true>(e, q2, q3, one);
-    const float2v m01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, false);
-    const float2v m23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, true);
-    uint32_t w = cvt2_fp4_f32<0>(0u, nv_nudged(f0, m01.x, m01.x * s, g, gain),
-                                 nv_nudged(f1, m01.y, m01.y * s, g, gain), one);
-    w = cvt2_fp4_f32<1>(w, nv_nudged(f2, m23.x, m23.x * s, g, gain), nv_nudged(f3, m23.y, m23.y * s, g, gain), one);
-    return b.zero ? 0u : (w & 0xFFFFu);
-  }
+  const float eighth = scale_operand(124u);                     // the conversion divides by 2^-3
+  const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.code, one, false)[0];
+  // min(|x| r_b, 8) / 8 as the product's clamp to [0, 1] (a NaN r_b, a zero
+  // block, gives 0; its codes are dropped below)
+  const float q0 = __builtin_amdgcn_fmed3f(__builtin_fabsf(f0) * b.rcp8, 0.0f, 1.0f);
+  const float q1 = __builtin_amdgcn_fmed3f(__builtin_fabsf(f1) * b.rcp8, 0.0f, 1.0f);
+  const float q2 = __builtin_amdgcn_fmed3f(__builtin_fabsf(f2) * b.rcp8, 0.0f, 1.0f);
+  const float q3 = __builtin_amdgcn_fmed3f(__builtin_fabsf(f3) * b.rcp8, 0.0f, 1.0f);
+  // nearest E4M3 values of 8 q (no overflow at 8); the two conversions fill all
+  // four bytes, so the register they start from is immaterial
+  uint32_t e = cvt2_f32<kE4M3, false>(__float_as_uint(q0), q0, q1, eighth);
+  e = cvt2_f32<kE4M3, true>(e, q2, q3, eighth);
+  const float2v m01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, false);
+  const float2v m23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, one, true);
+  uint32_t w = cvt2_fp4_f32<0>(e, nv_nudged(f0, m01.x, m01.x * s, g), nv_nudged(f1, m01.y, m01.y * s, g), one);
+  w = cvt2_fp4_f32<1>(w, nv_nudged(f2, m23.x, m23.x * s, g), nv_nudged(f3, m23.y, m23.y * s, g), one);
+  return b.zero ? 0u : (w & 0xFFFFu);
 }
 
 // One 16-element block decided entirely in FP64 (g outside [2^-90, 2^100], or
