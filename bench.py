@@ -218,7 +218,25 @@ def _requant_workload():
             "base": "fp4_in_fp8_requant_14336x4096", "title": "MXFP4 -> FP8 128x128 requantization, row + transposed "
                                                              "copy + spreads, 14336x4096",
             "kernels": [("requant_kernel<0, 0, true, true>", "requant_kernel<row+col>", rd, wr)], "dominant": 0,
-            "sources": COMMON_SOURCES + [CSRC + "mx_requant.hip", CSRC + "mx_cast_impl.h"], "cpu": None}
+            "sources": COMMON_SOURCES + [CSRC + "mx_requant.hip", CSRC + "mx_cast_impl.h"],
+            "cpu": {"gen": lambda dev, i: _gen("weights")(dev, 0).view(1, r, c), "shape": (1, r, c),
+                    "setup": _requant_setup, "slab": _requant_slab,
+                    "note": "the MXFP4 plane made by the oracle beforehand, untimed"}}
+
+
+def _requant_setup(x_bits):
+    """The oracle's MXFP4 plane of the weights (E2M1 1x32, floor), codes and
+    scales side by side: [1][R][C/2 + C/32] bytes."""
+    import numpy as np
+    import oracle as O
+    q = O.quantize(x_bits, "bf16", O.E2M1, O.FLOOR, O.ROW)
+    return np.concatenate([q["row_codes"], q["row_scales"]], axis=2)
+
+
+def _requant_slab(src, b, r0, n):
+    import oracle as O
+    half = src.shape[2] * 16 // 17                               # C/2 of the C/2 + C/32 bytes
+    O.requant_fp4_to_fp8(src[b:b + 1, r0:r0 + n, :half], src[b:b + 1, r0:r0 + n, half:])
 
 
 def _qat_workload():
@@ -251,7 +269,14 @@ def _qat_workload():
             "base": "qat_fp32_fp4_fp8_14336x4096", "title": desc,
             "kernels": [("requant_kernel<2, 0, true, true>", "requant_kernel<fp32 master,row+col>", rd, wr)],
             "dominant": 0, "sources": COMMON_SOURCES + [CSRC + "mx_requant.hip", CSRC + "mx_cast_impl.h"],
-            "cpu": None}
+            "cpu": {"gen": lambda dev, i: _gen("weights")(dev, 0).float().view(1, r, c), "shape": (1, r, c),
+                    "slab": _qat_slab}}
+
+
+def _qat_slab(x_bits, b, r0, n):
+    import oracle as O
+    q = O.quantize(x_bits[b, r0:r0 + n], "f32", O.E2M1, O.FLOOR, O.ROW)
+    O.requant_fp4_to_fp8(q["row_codes"], q["row_scales"])
 
 
 def _wide_range_pipeline():
@@ -600,6 +625,9 @@ def cpu_baselines(workload: str, dev, procs: int, single_budget_s: float = 10.0)
         return None, None
     B, R, C = cpu["shape"]
     x = I.to_bits(cpu["gen"](dev, 0)).reshape(B, R, C)
+    if "setup" in cpu:                     # the workload's own input, made by the oracle (untimed)
+        x = cpu["setup"](x)
+    note = f", {cpu['note']}" if "note" in cpu else ""
     ext = cpu.get("extrapolate", 1)
     per_row = wl["bytes"] / (B * ext * R)
     slab = 512
@@ -623,7 +651,7 @@ def cpu_baselines(workload: str, dev, procs: int, single_budget_s: float = 10.0)
         t_single = t_used + t_prep * frac
         single = {"value": round(per_row * done / t_single / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                   "sample": f"{done} rows of {B * R} ({'tensor batch of ' + str(B) if B > 1 else 'one tensor'}) in "
-                            f"512-row slabs, NumPy float64 oracle, one process, {t_single:.1f} s"}
+                            f"512-row slabs, NumPy float64 oracle, one process, {t_single:.1f} s{note}"}
         par = None
         if procs > 1:
             with mp.get_context("fork").Pool(procs) as pool:
@@ -635,11 +663,11 @@ def cpu_baselines(workload: str, dev, procs: int, single_budget_s: float = 10.0)
                 affinity = len(os.sched_getaffinity(0))
             except AttributeError:
                 affinity = None
-            note = (f"all {B * R} rows" if ext == 1 else
+            span = (f"all {B * R} rows" if ext == 1 else
                     f"{B} of {B * ext} tensors, timed and scaled x{ext} (extrapolated)")
             par = {"value": round(wl["bytes"] / (t * ext) / 1e9, 4), "unit": "GB/s", "cores": procs, "kind": "oracle",
-                   "sample": f"{note} in 512-row slabs over {procs} forked processes, NumPy float64 oracle, "
-                             f"{t:.2f} s",
+                   "sample": f"{span} in 512-row slabs over {procs} forked processes, NumPy float64 oracle, "
+                             f"{t:.2f} s{note}",
                    "extrapolated": ext != 1, "host_logical_cpus": os.cpu_count(), "affinity_cpus": affinity,
                    "cpu_model": _cpu_model(),
                    "procs_note": f"pool of min({CPU_PROCS}, host CPUs): {CPU_PROCS} processes are this GPU's share "
