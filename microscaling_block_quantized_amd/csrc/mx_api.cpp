@@ -138,7 +138,9 @@ int mx_quantize_ex(const void* x, mx_dtype x_dtype, mx_shape s, mx_fmt fmt, mx_s
       if (overlap(rs[i], rs[j])) return MX_ERR_ALIAS;
 
   const bool row_stream = axis == MX_AXIS_ROW && !b2d;
-  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, row_stream);
+  // the FP32 column-only stochastic-rounding kernel runs narrow tiles
+  const bool narrow = sr && !b2d && x_dtype == MX_F32 && axis == MX_AXIS_COL;
+  const mx::CastGrid g = mx::cast_grid(s.batch, s.rows, s.cols, row_stream, narrow);
   if (g.blocks > kMaxGrid) return MX_ERR_TOO_LARGE;
   // per-thread offsets inside a tile are 32-bit: 128 rows of FP32 and 256 column-plane rows
   if (s.cols >= (INT64_C(1) << 22) || (want_col && s.rows >= (INT64_C(1) << 23))) return MX_ERR_TOO_LARGE;

@@ -130,12 +130,24 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nb, uint32_t 
 // block (the wave's 32 rows x 32 columns) instead of per 1x32 block; the
 // column copy then shares the block's scale, and the scale planes are the
 // [R/32][C/32] grid and its transpose.
+//
+// The FP32 column-only cast with stochastic rounding uses narrow tiles (kNarrow
+// below): 128 x 128, each wave 32 rows x 64 columns, so a lane holds 8 rows of
+// 4 elements instead of 16. Its Philox draws and their decisions then fit two
+// workgroups per CU (at most 128 VGPRs) instead of one.
+template <bool BF16, int F, int M, int AX, int RD, bool B2>
+constexpr bool kNarrow = RD == kSr && !BF16 && AX == kCol && !B2;
+
 template <bool BF16, int F, int M, int AX, int RD, bool B2>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    RD == kSr ? 2 : (BF16 ? 4 : (AX == kBoth ? 2 : 3))))) void mx_cast_kernel(CastArgs a) {
+    kNarrow<BF16, F, M, AX, RD, B2> ? 4 : (RD == kSr ? 2 : (BF16 ? 4 : (AX == kBoth ? 2 : 3)))))) void
+mx_cast_kernel(CastArgs a) {
   constexpr int VEC = InC<BF16>::vec;          // elements per 16-byte chunk
   constexpr int ES = BF16 ? 2 : 4;             // input element bytes
-  constexpr int LPR = 128 / VEC;               // lanes per 128-column wave row: 16 | 32
+  constexpr bool NARROW = kNarrow<BF16, F, M, AX, RD, B2>;
+  constexpr int TC = NARROW ? kTileCNarrow : kTileC;   // tile columns: 256 | 128
+  constexpr int WCS = TC / kWaveCols;          // columns per wave: 128 | 64
+  constexpr int LPR = WCS / VEC;               // lanes per wave row: 16 | 32 (narrow FP32: 16)
   constexpr int RG = 64 / LPR;                 // row groups per wave: 4 | 2
   constexpr int RPT = 32 / RG;                 // rows per thread: 8 | 16
   constexpr int LPB = 32 / VEC;                // lanes per row block: 4 | 8
@@ -151,8 +163,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // kernel, where the extra registers would spill
   constexpr bool SRFAST = !(AX == kBoth && !BF16);
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
-  __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * kWaveRows : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? TC * BPC : 16];
+  __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? TC * kWaveRows : 4];
   // 4-bit codes with both copies: a wave row's row codes are only 64 bytes, half
   // of a 128-byte line whose other half comes from the neighbouring wave. They are
   // staged here as [tile row][128 bytes] and, after the barrier the column copy
@@ -183,10 +195,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   tile_coords(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_c, (a.flags & kStaggerStrips) != 0, bi, tr, tcol);
   const int64_t R = a.rows, C = a.cols;
   const int64_t r0 = int64_t(tr) * kTileR;
-  const int64_t c0 = int64_t(tcol) * kTileC;
+  const int64_t c0 = int64_t(tcol) * TC;
   // rows / columns of this tile inside the tensor (ragged last tiles)
   const int rows_in = int(min<int64_t>(R - r0, kTileR));
-  const int cols_in = int(min<int64_t>(C - c0, kTileC));
+  const int cols_in = int(min<int64_t>(C - c0, TC));
   const uint32_t Cu = uint32_t(C);             // host guarantees C < 2^22 and, for columns, R < 2^23
   const bool lines6 = ROWLDS6 && (Cu & 63u) == 0u;
   const bool rs8 = RS8 && (a.flags & kRowScaleQword) != 0;
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int wr = wid % kWaveRows, wc = wid / kWaveRows;
   const int lane = threadIdx.x & 63;
   const int q = lane / LPR, t = lane % LPR;
-  const int lcol = 128 * wc + t * VEC;                    // column inside the tile
+  const int lcol = WCS * wc + t * VEC;                    // column inside the tile
   const int lrow = 32 * wr + RPT * q;                     // first row of this thread inside the tile
   const bool col_ok = lcol < cols_in;
 
@@ -289,7 +301,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         for (int d = 0; d < 4; ++d) cm[d] = max(cm[d], (&v[k].x)[d] & 0x7FFFFFFFu);
       }
 #pragma unroll
-      for (int d = 0; d < 4; ++d) cm[d] = max_xor32(cm[d]);   // the 2 row groups of the 32-row block
+      for (int d = 0; d < 4; ++d) {                           // the row groups of the 32-row block
+        cm[d] = max_xor32(cm[d]);
+        if constexpr (RG == 4) cm[d] = max_xor16(cm[d]);
+      }
       if constexpr (B2) code2d = scale_code<F, M, false>(group_max<LPB>(max(max(cm[0], cm[1]), max(cm[2], cm[3]))));
       if constexpr (COLS) {
 #pragma unroll
@@ -456,11 +471,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
-        if constexpr (RB == 8) {
+        if constexpr (RPT == 16 && RB == 8) {
           *reinterpret_cast<uint4*>(lds_codes + stage_off(j)) = make_uint4(w[j][0], w[j][1], w[j][2], w[j][3]);
-        } else {
+        } else if constexpr (RPT == 16) {
           *reinterpret_cast<uint2*>(lds_codes + stage_off(j)) =
               make_uint2((w[j][0] & 0xFFFFu) | (w[j][1] << 16), (w[j][2] & 0xFFFFu) | (w[j][3] << 16));
+        } else if constexpr (RB == 8) {                          // narrow tiles: 8 rows
+          *reinterpret_cast<uint2*>(lds_codes + stage_off(j)) = make_uint2(w[j][0], w[j][1]);
+        } else {
+          *reinterpret_cast<uint32_t*>(lds_codes + stage_off(j)) = (w[j][0] & 0xFFFFu) | (w[j][1] << 16);
         }
       }
     }
@@ -492,11 +511,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           w[g] = encode4_f32<F, M>(__uint_as_float((&v[4 * g].x)[j]), __uint_as_float((&v[4 * g + 1].x)[j]),
                                    __uint_as_float((&v[4 * g + 2].x)[j]), __uint_as_float((&v[4 * g + 3].x)[j]),
                                    code_j[j]);
-        if constexpr (RB == 8) {
+        if constexpr (RPT == 16 && RB == 8) {
           *reinterpret_cast<uint4*>(lds_codes + off) = make_uint4(w[0], w[1], w[2], w[3]);   // 16 rows
-        } else {
+        } else if constexpr (RPT == 16) {
           *reinterpret_cast<uint2*>(lds_codes + off) =
               make_uint2((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16));
+        } else if constexpr (RB == 8) {                                                   // 8 rows
+          *reinterpret_cast<uint2*>(lds_codes + off) = make_uint2(w[0], w[1]);
+        } else {
+          *reinterpret_cast<uint32_t*>(lds_codes + off) = (w[0] & 0xFFFFu) | (w[1] << 16);
         }
       }
     }
@@ -515,7 +538,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const int64_t ctile_elem = (int64_t(bi) * C + c0) * R + r0;
     uint8_t* cct = reinterpret_cast<uint8_t*>(a.col_codes) + ctile_elem * CB / 8;
 #pragma unroll
-    for (int i = 0; i < kTileC * CPC / kThreads; ++i) {
+    for (int i = 0; i < TC * CPC / kThreads; ++i) {
       const int id = threadIdx.x + i * kThreads;
       const int cl = id / CPC;
       const int part = id % CPC;

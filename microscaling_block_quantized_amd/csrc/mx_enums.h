@@ -17,6 +17,7 @@ constexpr int kWaveRows = 4;
 constexpr int kWaveCols = 2;
 constexpr int kTileR = 32 * kWaveRows;       // 128
 constexpr int kTileC = 128 * kWaveCols;      // 256
+constexpr int kTileCNarrow = 64 * kWaveCols; // 128: the FP32 column-only cast with stochastic rounding
 constexpr int kThreads = 64 * kWaveRows * kWaveCols;
 // Row-only MX cast: 256-thread workgroups, kRowSteps 1 KiB steps per wave.
 constexpr int kRowThreads = 256;

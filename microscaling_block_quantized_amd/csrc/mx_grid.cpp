@@ -3,10 +3,11 @@
 
 namespace mx {
 
-CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, bool row_stream) {
+CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, bool row_stream, bool narrow) {
   CastGrid g;
+  const int64_t tc = narrow ? kTileCNarrow : kTileC;
   g.tiles_r = (rows + kTileR - 1) / kTileR;
-  g.tiles_c = (cols + kTileC - 1) / kTileC;
+  g.tiles_c = (cols + tc - 1) / tc;
   if (row_stream) {
     const int64_t per_block = int64_t(kRowThreads / 64) * 64 * kRowSteps * 8;   // elements (BF16 bound)
     g.blocks = (batch * rows * cols + per_block - 1) / per_block * 2;           // FP32 needs twice as many

@@ -59,7 +59,8 @@ struct CastGrid {
 
 // Launch geometry; `blocks` bounds the workgroup count of the chosen kernel:
 // the row-only stream kernel (row_stream) or the tiled one.
-CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, bool row_stream);
+// narrow: the FP32 column-only cast with stochastic rounding (kTileCNarrow-column tiles)
+CastGrid cast_grid(int64_t batch, int64_t rows, int64_t cols, bool row_stream, bool narrow = false);
 // Round-to-nearest-even, 1x32 blocks.
 hipError_t launch_cast(bool in_bf16, int fmt, int mode, int axis, const CastArgs& a,
                        uint32_t nblocks, hipStream_t s);
