@@ -448,13 +448,22 @@ mx_cast_kernel(CastArgs a) {
       return cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
     };
     if constexpr (SR && !BF16) {
-      // FP32 with stochastic rounding: 4 rows' draws at a time, all columns of them
+      // FP32 with stochastic rounding: 4 rows' draws at a time, all columns of them.
+      // Lanes t and t ^ 1 share one Philox block per row only when cols % 8 == 0; a
+      // column-only cast may have cols % 8 == 4, where every other row's blocks start
+      // at odd lanes, and each lane then draws its own rows' blocks.
+      const bool pairs = (Cu & 7u) == 0u;
       uint32_t w[VEC][RPT / 4];
 #pragma unroll
       for (int g = 0; g < RPT / 4; ++g) {
         uint32_t dr[4][VEC / 2];
-        row_draws_pair(4 * g, dr[0], dr[1]);
-        row_draws_pair(4 * g + 2, dr[2], dr[3]);
+        if (pairs) {
+          row_draws_pair(4 * g, dr[0], dr[1]);
+          row_draws_pair(4 * g + 2, dr[2], dr[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) row_draws(4 * g + r, dr[r]);
+        }
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const int e = int(code_j[j]) - 127;

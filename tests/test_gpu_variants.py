@@ -82,6 +82,34 @@ def test_sr_workloads(mx, fmt):
     check(mx, a, fmt, "floor", "both", "act/both", rounding="sr", seed=7)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_sr_column_only_narrow_tiles(mx, fmt):
+    """The FP32 column-only cast with stochastic rounding runs 128-column tiles
+    with 64-column waves: column counts of 36, 100, 300 and 132 (ragged last
+    tiles, waves with no columns, lanes past the tensor), batches, ragged tile
+    rows, FP32 edge blocks, both scale rules and both seeds; outputs start as a
+    sentinel and a guard band follows each plane."""
+    g = torch.Generator().manual_seed(44)
+    bits = OFMT[fmt].bits
+    cases = [(1, 64, 36), (2, 96, 100), (1, 160, 300), (3, 32, 132)]
+    for i, (b, r, c) in enumerate(cases):
+        x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-10, 10, (b, 1, c), generator=g).float())
+        mode = ("floor", "roundup")[i % 2]
+        seed = SEEDS[i % 2]
+        nc, ns = b * c * r * bits // 8, b * c * (r // 32)
+        cc = torch.full((nc + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+        cs = torch.full((ns + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+        got = mx.mx_quantize(x.cuda(), fmt, mode, "col", rounding="sr", seed=seed,
+                             out={"col_codes": cc[:nc].view(b, c, r * bits // 8), "col_scales": cs[:ns].view(b, c, r // 32)})
+        torch.cuda.synchronize()
+        same({k: v.cpu().numpy() for k, v in got.items()}, oracle(x, fmt, mode, "col", rounding="sr", seed=seed),
+             f"sr col-only {(b, r, c)}")
+        assert (cc[nc:].cpu() == 0xA5).all() and (cs[ns:].cpu() == 0xA5).all()
+    e = pad_rows(I.fp32_edges(fmt))
+    for mode in ("floor", "roundup"):
+        check(mx, e, fmt, mode, "col", "edges/col", rounding="sr", seed=SEEDS[1])
+
+
 def test_sr_draws_depend_on_seed_only(mx):
     x = I.gradients(256, 256, seed=43).cuda()
     a = mx.mx_quantize(x, "e2m1", "roundup", "col", rounding="sr", seed=5)
