@@ -284,6 +284,30 @@ __device__ __forceinline__ uint32_t nv_encode4(float f0, float f1, float f2, flo
   return b.zero ? 0u : (w & 0xFFFFu);
 }
 
+// Eight FP32 values of one block -> eight E2M1 codes filling a dword (element
+// i in bits 4i+3 .. 4i), each decided as in nv_encode4.
+__device__ __forceinline__ uint32_t nv_encode8(float f0, float f1, float f2, float f3, float f4, float f5, float f6,
+                                               float f7, const NvBlock& b, float g) {
+  const float one = scale_operand(127u);
+  const float eighth = scale_operand(124u);
+  const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.code, one, false)[0];
+  auto q = [&](float f) { return __builtin_amdgcn_fmed3f(__builtin_fabsf(f) * b.rcp8, 0.0f, 1.0f); };
+  const float q0 = q(f0), q1 = q(f1), q2 = q(f2), q3 = q(f3), q4 = q(f4), q5 = q(f5), q6 = q(f6), q7 = q(f7);
+  uint32_t e0 = cvt2_f32<kE4M3, false>(__float_as_uint(q0), q0, q1, eighth);
+  e0 = cvt2_f32<kE4M3, true>(e0, q2, q3, eighth);
+  uint32_t e1 = cvt2_f32<kE4M3, false>(__float_as_uint(q4), q4, q5, eighth);
+  e1 = cvt2_f32<kE4M3, true>(e1, q6, q7, eighth);
+  const float2v m01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e0, one, false);
+  const float2v m23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e0, one, true);
+  const float2v m45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e1, one, false);
+  const float2v m67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e1, one, true);
+  uint32_t w = cvt2_fp4_f32<0>(e0, nv_nudged(f0, m01.x, m01.x * s, g), nv_nudged(f1, m01.y, m01.y * s, g), one);
+  w = cvt2_fp4_f32<1>(w, nv_nudged(f2, m23.x, m23.x * s, g), nv_nudged(f3, m23.y, m23.y * s, g), one);
+  w = cvt2_fp4_f32<2>(w, nv_nudged(f4, m45.x, m45.x * s, g), nv_nudged(f5, m45.y, m45.y * s, g), one);
+  w = cvt2_fp4_f32<3>(w, nv_nudged(f6, m67.x, m67.x * s, g), nv_nudged(f7, m67.y, m67.y * s, g), one);
+  return b.zero ? 0u : w;
+}
+
 // One 16-element block decided entirely in FP64 (g outside [2^-90, 2^100], or
 // not a finite positive number): 16 elements at stride `step` elements from p,
 // the 8 code bytes to `codes` (8-byte aligned) and the scale byte to `scale`.
@@ -470,8 +494,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const bool ok = col_ok && lrow + k < rows_in;
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu / 2;
       if constexpr (BF16) {
-        const uint32_t w = nv_encode4(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), blk, g) |
-                           (nv_encode4(elem(k, 4), elem(k, 5), elem(k, 6), elem(k, 7), blk, g) << 16);
+        const uint32_t w = nv_encode8(elem(k, 0), elem(k, 1), elem(k, 2), elem(k, 3), elem(k, 4), elem(k, 5),
+                                      elem(k, 6), elem(k, 7), blk, g);
         if constexpr (ROWLDS) *reinterpret_cast<uint32_t*>(lds_rows + rows_off(lrow + k, lcol)) = w;
         else if (ok) store_nt4(dst, w);
       } else {
@@ -513,15 +537,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int cl = lcol + j;
       const int off = cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
       if constexpr (BF16) {
-        const uint32_t w = nv_encode4(elem(0, j), elem(1, j), elem(2, j), elem(3, j), cb[j], g) |
-                           (nv_encode4(elem(4, j), elem(5, j), elem(6, j), elem(7, j), cb[j], g) << 16);
+        const uint32_t w = nv_encode8(elem(0, j), elem(1, j), elem(2, j), elem(3, j), elem(4, j), elem(5, j),
+                                      elem(6, j), elem(7, j), cb[j], g);
         *reinterpret_cast<uint32_t*>(lds_codes + off) = w;               // 8 rows in 4 bytes
       } else {
-        uint32_t w[4];
+        uint32_t w[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          w[g4] = nv_encode4(elem(4 * g4, j), elem(4 * g4 + 1, j), elem(4 * g4 + 2, j), elem(4 * g4 + 3, j), cb[j], g);
-        *reinterpret_cast<uint2*>(lds_codes + off) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+        for (int h8 = 0; h8 < 2; ++h8)
+          w[h8] = nv_encode8(elem(8 * h8, j), elem(8 * h8 + 1, j), elem(8 * h8 + 2, j), elem(8 * h8 + 3, j),
+                             elem(8 * h8 + 4, j), elem(8 * h8 + 5, j), elem(8 * h8 + 6, j), elem(8 * h8 + 7, j), cb[j], g);
+        *reinterpret_cast<uint2*>(lds_codes + off) = make_uint2(w[0], w[1]);
       }
     }
     // column block index inside the tile: 16-row groups

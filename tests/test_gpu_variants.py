@@ -82,18 +82,22 @@ def test_sr_workloads(mx, fmt):
     check(mx, a, fmt, "floor", "both", "act/both", rounding="sr", seed=7)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("fmt", FMTS)
-def test_sr_column_only_narrow_tiles(mx, fmt):
-    """The FP32 column-only cast with stochastic rounding runs 128-column tiles
-    with 64-column waves: column counts of 36, 100, 300 and 132 (ragged last
-    tiles, waves with no columns, lanes past the tensor), batches, ragged tile
-    rows, FP32 edge blocks, both scale rules and both seeds; outputs start as a
-    sentinel and a guard band follows each plane."""
+def test_sr_column_only_ragged_cols(mx, fmt, dt):
+    """Column-only casts with stochastic rounding and column counts that are not
+    multiples of 32: FP32 (128-column tiles with 64-column waves) with 36, 100,
+    300 and 132 columns, where every other row's Philox blocks start mid-lane-
+    pair; BF16 with 40, 104, 264 and 136. Ragged last tiles, waves with no
+    columns, batches, ragged tile rows, both scale rules and both seeds; FP32
+    edge blocks; outputs start as a sentinel and a guard band follows each plane."""
     g = torch.Generator().manual_seed(44)
     bits = OFMT[fmt].bits
-    cases = [(1, 64, 36), (2, 96, 100), (1, 160, 300), (3, 32, 132)]
+    cases = ([(1, 64, 36), (2, 96, 100), (1, 160, 300), (3, 32, 132)] if dt == "f32" else
+             [(1, 64, 40), (2, 96, 104), (1, 160, 264), (3, 32, 136)])
     for i, (b, r, c) in enumerate(cases):
         x = torch.randn((b, r, c), generator=g) * torch.exp2(torch.randint(-10, 10, (b, 1, c), generator=g).float())
+        x = x.to(torch.bfloat16) if dt == "bf16" else x
         mode = ("floor", "roundup")[i % 2]
         seed = SEEDS[i % 2]
         nc, ns = b * c * r * bits // 8, b * c * (r // 32)
@@ -105,7 +109,7 @@ def test_sr_column_only_narrow_tiles(mx, fmt):
         same({k: v.cpu().numpy() for k, v in got.items()}, oracle(x, fmt, mode, "col", rounding="sr", seed=seed),
              f"sr col-only {(b, r, c)}")
         assert (cc[nc:].cpu() == 0xA5).all() and (cs[ns:].cpu() == 0xA5).all()
-    e = pad_rows(I.fp32_edges(fmt))
+    e = pad_rows(I.fp32_edges(fmt) if dt == "f32" else I.bf16_edges(fmt))
     for mode in ("floor", "roundup"):
         check(mx, e, fmt, mode, "col", "edges/col", rounding="sr", seed=SEEDS[1])
 
