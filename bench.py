@@ -528,7 +528,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str, workload: s
 
 # main kernel and element count of the workloads with SQ (instruction) counter summaries
 SQ_ELEMENTS = {"activations": 16384 * 4096, "act_e2m3": 16384 * 4096, "act_nvfp4": 16384 * 4096,
-               "grad_sr_e2m1": 8192 * 8192}
+               "grad_sr_e2m1": 8192 * 8192, "weights_fp4_in_fp8": 14336 * 4096, "qat_fp4_fp8": 14336 * 4096}
 SQ_PROFILE = os.path.join(ROOT, "profiles", "valu_lds_counters.md")
 SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
                "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR")
