@@ -12,7 +12,9 @@
 // column copy is the row-wise quantization of X^T.
 //
 // Work decomposition (gfx950, 64-wide waves). A workgroup of 8 waves owns a
-// 128-row x 256-column tile of one batch slice and reads it from HBM once:
+// 128-row x 256-column tile of one batch slice and reads it from HBM once (the
+// FP32 column-only cast with stochastic rounding: 128 x 128, each wave 64
+// columns wide, see kNarrow):
 //   * wave w = 4 * wc + wr covers rows 32*wr .. +31 and columns 128*wc .. +127;
 //     lane = q * LPR + t, where t picks a 16-byte chunk of a row (8 BF16 or
 //     4 FP32 elements) and q a group of RPT consecutive rows. One wave thus
