@@ -155,6 +155,26 @@ __device__ __forceinline__ NvScale nv_scale(float g) {
   return s;
 }
 
+// The block a partner lane computed: code and reciprocal arrive through a lane
+// exchange, the zero flag is recomputed.
+__device__ __forceinline__ NvBlock nv_block_of(uint32_t code, uint32_t rcp_bits) {
+  NvBlock b;
+  b.code = code;
+  b.rcp8 = __uint_as_float(rcp_bits);
+  b.zero = b.rcp8 != b.rcp8;
+  return b;
+}
+
+// c ? x : y, field by field (one select each; a select of whole structs can
+// end up in private memory)
+__device__ __forceinline__ NvBlock nv_pick(bool c, const NvBlock& x, const NvBlock& y) {
+  NvBlock r;
+  r.code = c ? x.code : y.code;
+  r.rcp8 = c ? x.rcp8 : y.rcp8;
+  r.zero = c ? x.zero : y.zero;
+  return r;
+}
+
 // UE4M3 value of code c (0 .. 0x7E) in FP64: subnormals m * 2^-9, normals (8 + m) * 2^(e - 10).
 __device__ __forceinline__ double ue4m3_value(uint32_t c) {
   const uint32_t e = c >> 3, m = c & 7u;
@@ -455,10 +475,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], (&v[k].x)[d] & 0x7FFF7FFFu);
       }
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        cm[d] = pk_max_xor16(cm[d]);                     // row groups q and q ^ 1
-        cb[2 * d] = nv_block((cm[d] & 0xFFFFu) << 16, sc, lds_rtab);
-        cb[2 * d + 1] = nv_block(cm[d] & 0xFFFF0000u, sc, lds_rtab);
+      for (int d = 0; d < 4; ++d) cm[d] = pk_max_xor16(cm[d]);   // row groups q and q ^ 1
+      // Row groups q and q ^ 1 share their 8 column blocks: the even one codes
+      // blocks 0..3, the odd one 4..7, and they swap the results. v_permlane16_swap
+      // of (x, x) gives, in an even 16-lane row, (own, partner) and in an odd
+      // one (partner, own).
+      const bool qodd = (q & 1) != 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        auto amag = [&](int jj) { return (jj & 1) ? (cm[jj >> 1] & 0xFFFF0000u) : (cm[jj >> 1] << 16); };
+        const uint32_t a_lo = amag(j), a_hi = amag(j + 4);
+        const NvBlock mine = nv_block(qodd ? a_hi : a_lo, sc, lds_rtab);
+        const auto xc = __builtin_amdgcn_permlane16_swap(mine.code, mine.code, false, false);
+        const uint32_t rb = __float_as_uint(mine.rcp8);
+        const auto xr = __builtin_amdgcn_permlane16_swap(rb, rb, false, false);
+        const NvBlock other = nv_block_of(qodd ? uint32_t(xc[0]) : uint32_t(xc[1]),
+                                          qodd ? uint32_t(xr[0]) : uint32_t(xr[1]));
+        cb[j] = nv_pick(qodd, other, mine);
+        cb[j + 4] = nv_pick(qodd, mine, other);
       }
     } else {
 #pragma unroll
@@ -478,19 +512,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     // the scale dword of blocks 4d .. 4d+3 of the wave's 128 columns, stored by lane t = HALF * d
     const int dcol = 128 * wc + 64 * (t / HALF);
     uint8_t* sdst = a.row_scales + ((int64_t(bi) * R + r0 + lrow) * C + c0 + dcol) / 16;
+    // BF16: lanes t and t ^ 1 hold the two halves of each row block; of a pair of
+    // rows the even lane codes the first block and the odd lane the second, and
+    // they swap the results (the second waits in `pend` for the next row)
+    auto bf16_row_max = [&](int k) {
+      const uint32_t h = pk_max_u16(pk_max_u16(v[k].x & 0x7FFF7FFFu, v[k].y & 0x7FFF7FFFu),
+                                    pk_max_u16(v[k].z & 0x7FFF7FFFu, v[k].w & 0x7FFF7FFFu));
+      const uint32_t m = max(h & 0xFFFFu, h >> 16) << 16;
+      return max(m, dpp<kDppXor1>(m));
+    };
+    NvBlock pend;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      uint32_t m;
+      NvBlock blk;
       if constexpr (BF16) {
-        const uint32_t h = pk_max_u16(pk_max_u16(v[k].x & 0x7FFF7FFFu, v[k].y & 0x7FFF7FFFu),
-                                      pk_max_u16(v[k].z & 0x7FFF7FFFu, v[k].w & 0x7FFF7FFFu));
-        m = max(h & 0xFFFFu, h >> 16) << 16;
-        m = max(m, dpp<kDppXor1>(m));
+        if ((k & 1) == 0) {
+          // both maxima on every lane first: each takes a lane exchange, which the
+          // partner lane must execute too
+          const bool todd = (t & 1) != 0;
+          const uint32_t m0 = bf16_row_max(k), m1 = bf16_row_max(k + 1);
+          const NvBlock mine = nv_block(todd ? m1 : m0, sc, lds_rtab);
+          const NvBlock other = nv_block_of(dpp<kDppXor1>(mine.code), dpp<kDppXor1>(__float_as_uint(mine.rcp8)));
+          blk = nv_pick(todd, other, mine);
+          pend = nv_pick(todd, mine, other);
+        } else {
+          blk = pend;
+        }
       } else {
-        m = max(max(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu), max(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu));
+        uint32_t m = max(max(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu), max(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu));
         m = group_max<4>(m);
+        blk = nv_block(m, sc, lds_rtab);
       }
-      const NvBlock blk = nv_block(m, sc, lds_rtab);
       const bool ok = col_ok && lrow + k < rows_in;
       uint8_t* dst = rct + rcoff + uint32_t(k) * Cu / 2;
       if constexpr (BF16) {
