@@ -583,21 +583,33 @@ def summarize_sq(command: str, csvs: list) -> str:
 # ---------------------------------------------------------------------------
 
 def _cpu_model() -> str:
+    """The host CPU as lscpu describes it: the model name (which a virtual machine
+    may shorten, e.g. to "AMD EPYC") with the family / model / stepping numbers
+    and the topology that identify it."""
+    info = {}
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
         for line in out.splitlines():
-            if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info[k.strip()] = v.strip()
     except (OSError, subprocess.SubprocessError):
         pass
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
+    name = info.get("Model name")
+    if not name:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        name = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    fields = [("family", "CPU family"), ("model", "Model"), ("stepping", "Stepping"), ("sockets", "Socket(s)"),
+              ("cores/socket", "Core(s) per socket"), ("threads/core", "Thread(s) per core"),
+              ("max MHz", "CPU max MHz")]
+    extra = ", ".join(f"{label} {info[key]}" for label, key in fields if info.get(key))
+    return f"{name or 'unknown'} ({extra})" if extra else (name or "unknown")
 
 
 _CPU_JOB = None
