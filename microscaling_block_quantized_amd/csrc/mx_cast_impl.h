@@ -548,13 +548,31 @@ mx_cast_kernel(CastArgs a) {
     const uint32_t cpitch = Ru * CB / 8;              // column-plane row pitch in bytes (< 2^23)
     const int64_t ctile_elem = (int64_t(bi) * C + c0) * R + r0;
     uint8_t* cct = reinterpret_cast<uint8_t*>(a.col_codes) + ctile_elem * CB / 8;
+    // Every staged chunk, this thread's column-scale dword and its row-scale word are read
+    // from LDS before the first store (all these LDS addresses exist whatever the tile's
+    // extent), so the reads overlap instead of each waiting behind the previous store.
+    constexpr int NWO = TC * CPC / kThreads;
+    uint4 wo[NWO];
 #pragma unroll
-    for (int i = 0; i < TC * CPC / kThreads; ++i) {
+    for (int i = 0; i < NWO; ++i) {
+      const int id = threadIdx.x + i * kThreads;
+      const int cl = id / CPC, part = id % CPC;
+      wo[i] = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+    }
+    const uint32_t col_scale_dw =
+        B2 ? 0u : *reinterpret_cast<const uint32_t*>(lds_scales + (threadIdx.x & (TC - 1)) * kWaveRows);
+    uint2 row_scale_qw = make_uint2(0u, 0u);
+    if constexpr (RS8) {
+      const int rl = threadIdx.x & (kTileR - 1);
+      row_scale_qw = make_uint2(lds_rs[2 * rl], lds_rs[2 * rl + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < NWO; ++i) {
       const int id = threadIdx.x + i * kThreads;
       const int cl = id / CPC;
       const int part = id % CPC;
       if (cl < cols_in && part * ROWS_PER_CHUNK < rows_in) {
-        const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+        const uint4 w = wo[i];
         uint8_t* dst = cct + uint32_t(cl) * cpitch + uint32_t(part) * OUT_CHUNK;
         if constexpr (CB == 6) {
           const uint3 p = pack6x16(w.x, w.y, w.z, w.w);
@@ -568,8 +586,8 @@ mx_cast_kernel(CastArgs a) {
       // the staged row scales: one 8-byte word (256 columns) per tile row
       const int rl = threadIdx.x;
       uint8_t* dst = a.row_scales + tile_elem / 32 + uint32_t(rl) * (Cu / 32);
-      if constexpr (CB == 6) store_sc1_8(dst, lds_rs[2 * rl], lds_rs[2 * rl + 1]);
-      else *reinterpret_cast<uint2*>(dst) = make_uint2(lds_rs[2 * rl], lds_rs[2 * rl + 1]);
+      if constexpr (CB == 6) store_sc1_8(dst, row_scale_qw.x, row_scale_qw.y);
+      else *reinterpret_cast<uint2*>(dst) = row_scale_qw;
     }
     if (lines6) {
       // the staged 6-bit row codes: 12 chunks of 16 bytes per tile row, through L2
@@ -622,7 +640,7 @@ mx_cast_kernel(CastArgs a) {
       const int cl = threadIdx.x;
       uint8_t* dst = a.col_scales + ctile_elem / 32 + uint32_t(cl) * Ru / 32;
       if (a.flags & kColScaleDword) {
-        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scales + cl * kWaveRows);
+        *reinterpret_cast<uint32_t*>(dst) = col_scale_dw;
       } else {
 #pragma unroll
         for (int w = 0; w < kWaveRows; ++w)
