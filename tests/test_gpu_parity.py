@@ -351,3 +351,24 @@ def test_tall_column_plane_addressing(mx, fmt):
     for r0 in ((1 << 22) - 128, R - 256):
         slab_check(out, x[r0:r0 + 256].cpu(), r0, fmt, "floor", "both")
     del out, x
+
+
+@pytest.mark.parametrize("fmt,dt,rows", [("e4m3", "bf16", 160), ("e4m3", "bf16", 256), ("e2m1", "bf16", 256),
+                                         ("e4m3", "f32", 256)])
+def test_widest_row_plane_addressing(mx, fmt, dt, rows):
+    """2^22 - 256 columns (the widest the ABI takes), so a tile's rows of the row plane
+    span 128 x C bytes: every plane compared in the first and last 512 columns, all rows.
+    160 rows: a ragged last tile and byte column scales; 256 rows: dword column scales."""
+    R, C = rows, (1 << 22) - 256
+    x = (I.activations(R, C, seed=41, device="cuda") if dt == "bf16"
+         else I.gradients(R, C, seed=41, device="cuda"))
+    out = mx.mx_quantize(x, fmt, "floor", "both")
+    torch.cuda.synchronize()
+    bits = OFMT[fmt].bits
+    for c0 in (0, C - 512):
+        exp = oracle_quant(x[:, c0:c0 + 512].cpu(), fmt, "floor", "both")
+        got = {"row_codes": out["row_codes"][:, c0 * bits // 8:(c0 + 512) * bits // 8],
+               "row_scales": out["row_scales"][:, c0 // 32:(c0 + 512) // 32],
+               "col_codes": out["col_codes"][c0:c0 + 512], "col_scales": out["col_scales"][c0:c0 + 512]}
+        assert_same({k: v.cpu().numpy() for k, v in got.items()}, exp, f"columns {c0}..+512")
+    del out, x
