@@ -200,7 +200,9 @@ mx_cast_kernel(CastArgs a) {
   constexpr bool SRFAST = !(AX == kBoth && !BF16);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? TC * BPC : 16];
-  __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? TC * kWaveRows : 4];
+  // column-block scale codes as [wave row][tile column]: a lane's codes of its VEC
+  // columns are contiguous and leave in one store
+  __shared__ __attribute__((aligned(8))) uint8_t lds_scales[COLS ? TC * kWaveRows : 8];
   // 4-bit codes with both copies: a wave row's row codes are only 64 bytes, half
   // of a 128-byte line whose other half comes from the neighbouring wave. They are
   // staged here as [tile row][128 bytes] and, after the barrier the column copy
@@ -496,9 +498,15 @@ mx_cast_kernel(CastArgs a) {
     // encode column j of this thread (rows lrow .. +RPT-1) and stage it at
     // [column][row], the 16-byte chunk index XORed with (column / 8) mod CPC
     const int byte0 = lrow * RB / 8;                  // this thread's offset inside a staged column
+    // With 8-byte staging writes (8 rows of 1-byte codes), the 16 lanes of a quarter-wave
+    // write 16 columns, and columns 64 apart take the same chunk swizzle: the upper 64
+    // columns of each 128 therefore use the other 8-byte half of every chunk (swapped
+    // back on the way out), so that a quarter-wave covers all banks once.
+    constexpr bool SUBSWZ = RPT * RB / 8 == 8;
     auto stage_off = [&](int j) {
       const int cl = lcol + j;
-      return cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
+      const int half = SUBSWZ ? ((cl >> 6) & 1) << 3 : 0;
+      return cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | ((byte0 & 15) ^ half));
     };
     if constexpr (SR && !BF16) {
       // FP32 with stochastic rounding: 4 rows' draws at a time, all columns of them.
@@ -586,8 +594,14 @@ mx_cast_kernel(CastArgs a) {
       }
     }
     if (q == 0) {
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) lds_scales[(lcol + j) * kWaveRows + wr] = uint8_t(code_j[j]);
+      if constexpr (VEC == 8) {
+        *reinterpret_cast<uint2*>(lds_scales + wr * TC + lcol) =
+            make_uint2(pack_low_bytes(code_j[0], code_j[1], code_j[2], code_j[3]),
+                       pack_low_bytes(code_j[4], code_j[5], code_j[6], code_j[7]));
+      } else {
+        *reinterpret_cast<uint32_t*>(lds_scales + wr * TC + lcol) =
+            pack_low_bytes(code_j[0], code_j[1], code_j[2], code_j[3]);
+      }
     }
     __syncthreads();
 
@@ -608,10 +622,19 @@ mx_cast_kernel(CastArgs a) {
     for (int i = 0; i < NWO; ++i) {
       const int id = threadIdx.x + i * kThreads;
       const int cl = id / CPC, part = id % CPC;
-      wo[i] = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+      const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+      // the chunk halves of the upper 64 columns of each 128 (SUBSWZ); with 512 threads and
+      // 8 chunks per column, column cl = (threadIdx.x + 512 i) / 8 has (cl / 64) & 1 == i & 1
+      const bool swap = SUBSWZ && ((CPC == 8 && kThreads == 512) ? (i & 1) != 0 : ((cl >> 6) & 1) != 0);
+      wo[i] = swap ? make_uint4(w.z, w.w, w.x, w.y) : w;
     }
-    const uint32_t col_scale_dw =
-        B2 ? 0u : *reinterpret_cast<const uint32_t*>(lds_scales + (threadIdx.x & (TC - 1)) * kWaveRows);
+    // the column's 4 block codes (one per wave row), byte w for rows 32 w .. 32 w + 31
+    auto col_codes4 = [&](int c) {
+      return uint32_t(lds_scales[c]) | (uint32_t(lds_scales[TC + c]) << 8) | (uint32_t(lds_scales[2 * TC + c]) << 16) |
+             (uint32_t(lds_scales[3 * TC + c]) << 24);
+    };
+    static_assert(kWaveRows == 4, "a column's block codes fill one dword");
+    const uint32_t col_scale_dw = B2 ? 0u : col_codes4(int(threadIdx.x & (TC - 1)));
     uint2 row_scale_qw = make_uint2(0u, 0u);
     if constexpr (RS8) {
       const int rl = threadIdx.x & (kTileR - 1);
@@ -693,11 +716,11 @@ mx_cast_kernel(CastArgs a) {
         const int64_t nbr = R / 32;
         uint8_t* dst = a.col_scales + (int64_t(bi) * (C / 32) + c0 / 32 + cb) * nbr + r0 / 32;
         if (a.flags & kColScaleDword) {
-          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scales + 32 * cb * kWaveRows);
+          *reinterpret_cast<uint32_t*>(dst) = col_codes4(32 * cb);
         } else {
 #pragma unroll
           for (int w = 0; w < kWaveRows; ++w)
-            if (32 * w < rows_in) dst[w] = lds_scales[32 * cb * kWaveRows + w];
+            if (32 * w < rows_in) dst[w] = lds_scales[w * TC + 32 * cb];
         }
       }
     } else if (a.flags & kColScaleDword) {
@@ -710,7 +733,7 @@ mx_cast_kernel(CastArgs a) {
       uint8_t* dst = a.col_scales + ctile_elem / 32 + uint32_t(cl) * Ru / 32;
 #pragma unroll
       for (int w = 0; w < kWaveRows; ++w)
-        if (32 * w < rows_in) dst[w] = lds_scales[cl * kWaveRows + w];
+        if (32 * w < rows_in) dst[w] = lds_scales[w * TC + cl];
     }
   }
 }
