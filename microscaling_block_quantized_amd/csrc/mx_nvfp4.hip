@@ -374,7 +374,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   constexpr int SPC = kTileR / 16;             // column blocks (scales) per tile column: 8
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_codes[COLS ? kTileC * BPC : 16];
-  __shared__ __attribute__((aligned(4))) uint8_t lds_scales[COLS ? kTileC * SPC : 4];
+  // column-block scale codes as [16-row group][tile column]: a lane's codes of its VEC
+  // columns are contiguous and leave in one store
+  __shared__ __attribute__((aligned(8))) uint8_t lds_scales[COLS ? kTileC * SPC : 8];
   __shared__ float lds_rtab[kNvTab];
   // With both copies, a wave row's row codes (64 bytes, half of a 128-byte line) are
   // staged as [tile row][128 bytes] and written as whole lines after the barrier the
@@ -603,8 +605,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     }
     // column block index inside the tile: 16-row groups
     if (BF16 ? (q % 2 == 0) : true) {
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) lds_scales[(lcol + j) * SPC + lrow / 16] = uint8_t(cb[j].code);
+      if constexpr (VEC == 8) {
+        *reinterpret_cast<uint2*>(lds_scales + (lrow / 16) * kTileC + lcol) =
+            make_uint2(pack_low_bytes(cb[0].code, cb[1].code, cb[2].code, cb[3].code),
+                       pack_low_bytes(cb[4].code, cb[5].code, cb[6].code, cb[7].code));
+      } else {
+        *reinterpret_cast<uint32_t*>(lds_scales + (lrow / 16) * kTileC + lcol) =
+            pack_low_bytes(cb[0].code, cb[1].code, cb[2].code, cb[3].code);
+      }
     }
     __syncthreads();
 
@@ -662,12 +670,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int cl = threadIdx.x;
       uint8_t* dst = a.col_scales + ctile_elem / 16 + uint32_t(cl) * Ru / 16;
       if ((a.flags & kColScaleDword) && rows_in == kTileR) {
-        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scales + cl * SPC);
-        *reinterpret_cast<uint32_t*>(dst + 4) = *reinterpret_cast<const uint32_t*>(lds_scales + cl * SPC + 4);
+        auto codes4 = [&](int s0) {
+          return uint32_t(lds_scales[s0 * kTileC + cl]) | (uint32_t(lds_scales[(s0 + 1) * kTileC + cl]) << 8) |
+                 (uint32_t(lds_scales[(s0 + 2) * kTileC + cl]) << 16) | (uint32_t(lds_scales[(s0 + 3) * kTileC + cl]) << 24);
+        };
+        *reinterpret_cast<uint32_t*>(dst) = codes4(0);
+        *reinterpret_cast<uint32_t*>(dst + 4) = codes4(4);
       } else {
 #pragma unroll
         for (int s = 0; s < SPC; ++s)
-          if (16 * s < rows_in) dst[s] = lds_scales[cl * SPC + s];
+          if (16 * s < rows_in) dst[s] = lds_scales[s * kTileC + cl];
       }
     }
   }
