@@ -589,7 +589,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
       const int cl = lcol + j;
-      const int off = cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | (byte0 & 15));
+      // BF16: 4-byte writes; the 4-byte slot inside a chunk is XORed with (column / 32) mod 4 so
+      // that a quarter-wave's 16 columns reach 16 different banks
+      const int slot = BF16 ? ((cl >> 5) & 3) << 2 : 0;
+      const int off = cl * BPC + ((((byte0 >> 4) ^ ((cl >> 3) & (CPC - 1))) << 4) | ((byte0 & 15) ^ slot));
       if constexpr (BF16) {
         const uint32_t w = nv_encode8(elem(0, j), elem(1, j), elem(2, j), elem(3, j), elem(4, j), elem(5, j),
                                       elem(6, j), elem(7, j), cb[j], g);
@@ -626,7 +629,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
       const int cl = id / CPC;
       const int part = id % CPC;                      // rows 32 part .. +31
       if (cl < cols_in && 32 * part < rows_in) {
-        const uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+        uint4 w = *reinterpret_cast<const uint4*>(lds_codes + cl * BPC + ((part ^ ((cl >> 3) & (CPC - 1))) << 4));
+        if constexpr (BF16) {
+          // undo the slot XOR: column cl = (threadIdx.x + 512 i) / 4 has (cl / 32) mod 4 = (threadIdx.x / 128) mod 4
+          const int p = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 7) & 3);
+          if (p & 1) w = make_uint4(w.y, w.x, w.w, w.z);
+          if (p & 2) w = make_uint4(w.z, w.w, w.x, w.y);
+        }
         uint8_t* dst = cct + uint32_t(cl) * cpitch + uint32_t(part) * 16;
         if (32 * part + 32 > rows_in) {
           store_nt8(dst, make_uint2(w.x, w.y));        // a 16-row tail
