@@ -387,7 +387,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
   // Row scales of full-width tiles (kNvRowScaleWords): a tile row's 16 scale
   // bytes (4 dwords from 2 waves) are staged and leave as one 16-byte store
   // after the barrier.
-  __shared__ __attribute__((aligned(16))) uint32_t lds_rs[ROWLDS ? kTileR * 4 : 4];
+  // one row's 4 scale dwords at a 5-dword pitch: the 8 lanes storing rows 8 apart then reach
+  // different banks
+  __shared__ __attribute__((aligned(16))) uint32_t lds_rs[ROWLDS ? kTileR * 5 : 4];
   auto rows_off = [](int r, int c) { return r * (kTileC / 2) + ((c / 2) ^ (((r >> 3) & 7) << 4)); };
 
   uint32_t bi, tr, tcol;
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
         sb |= dpp<kDppRor8>(sb);
       }
       if (rs16) {
-        if (t % HALF == 0) lds_rs[(lrow + k) * 4 + dcol / 64] = sb;
+        if (t % HALF == 0) lds_rs[(lrow + k) * 5 + dcol / 64] = sb;
       } else if (t % HALF == 0 && lrow + k < rows_in && dcol < cols_in) {
         uint8_t* dst = sdst + int64_t(k) * C / 16;
         if (a.flags & kRowScaleDword) {
@@ -673,7 +675,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 ?
     if (rs16 && int(threadIdx.x) < rows_in) {
       const int rl = threadIdx.x;
       uint8_t* dst = a.row_scales + ((int64_t(bi) * R + r0 + rl) * C + c0) / 16;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(lds_rs + rl * 4);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lds_rs[rl * 5], lds_rs[rl * 5 + 1], lds_rs[rl * 5 + 2], lds_rs[rl * 5 + 3]);
     }
     if (int(threadIdx.x) < cols_in) {
       const int cl = threadIdx.x;
